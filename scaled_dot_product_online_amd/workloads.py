@@ -1,0 +1,44 @@
+"""The attention workloads that the tests and the benchmark run (shapes only).
+
+Each entry is (name, B, Hq, Hkv, Lq, Lkv, D, dtype, is_causal). Sources:
+* ``fp32_tiny`` and ``fp32_b8h8s128`` — PyTensor issue "PERF: detect
+  scaled-dot-product-attention pattern ...", section "Reproducer + metrics"
+  (B, H, S, hd = 8, 8, 128, 64, float32, seed 0); the tiny case is a reduced copy
+  of it for an oracle that finishes in well under a second.
+* ``fp16_h8_*`` — mps-flash-sdpa 0.1.0, sections "Quick Start" ([1, 8, 2048, 64]
+  fp16, causal on and off) and "Benchmarks" (sequence 2048 and 4096).
+* ``bf16_gqa8_causal_4k_d128`` — grouped-query attention with causal masking
+  (MLX pull request "[Metal] Add Flash Attention VJP for training", sections
+  "Key Features" and "Test Plan": GQA 8:1) at a long-context training shape.
+* ``vec_*`` — the short-query path (same pull request, "Implementation Notes",
+  vector VJP for L <= 8) with Lq != Lkv ("Test Plan", edge cases).
+"""
+
+from __future__ import annotations
+
+WORKLOADS = [
+    ("fp32_tiny", 1, 2, 2, 64, 64, 32, "f32", False),
+    ("fp32_b8h8s128", 8, 8, 8, 128, 128, 64, "f32", False),
+    ("fp16_h8_2k", 1, 8, 8, 2048, 2048, 64, "f16", False),
+    ("fp16_h8_2k_causal", 1, 8, 8, 2048, 2048, 64, "f16", True),
+    ("fp16_h8_4k", 1, 8, 8, 4096, 4096, 64, "f16", False),
+    ("fp16_h8_4k_causal", 1, 8, 8, 4096, 4096, 64, "f16", True),
+    ("bf16_gqa8_causal_4k_d128", 4, 32, 4, 4096, 4096, 128, "bf16", True),
+]
+for _dt in ("f16", "bf16"):
+    for _lq in (1, 4, 8):
+        for _d in (64, 128):
+            WORKLOADS.append((f"vec_{_dt}_lq{_lq}_d{_d}", 16, 32, 8, _lq, 8192, _d, _dt, False))
+
+BY_NAME = {w[0]: w for w in WORKLOADS}
+
+# The workload the headline throughput is quoted on.
+HEADLINE = "bf16_gqa8_causal_4k_d128"
+
+
+def flops(B, Hq, Lq, Lkv, D, is_causal, backward=False):
+    """Counted FLOPs: 4*B*Hq*Lq*Lkv*D forward, 2.5x that for the backward, halved when causal."""
+    f = 4.0 * B * Hq * Lq * Lkv * D
+    if backward:
+        f *= 2.5
+    return f / 2 if is_causal else f
