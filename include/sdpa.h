@@ -1,0 +1,134 @@
+/*
+ * sdpa.h — fused scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libsdpa_mi355x.so. The library computes
+ *
+ *     O = softmax((Q K^T) * scale [+ causal mask]) V
+ *
+ * and its gradients, with grouped-query attention (GQA). The forward is the
+ * definition in the PyTensor issue "PERF: detect scaled-dot-product-attention
+ * pattern and lower to mx.fast.scaled_dot_product_attention" (section "Sketch":
+ * scores (Q K^T) * scale, row-max subtraction, exponentials normalised by their
+ * row sum, times V); causal masking and the [B, H, S, D] layout follow
+ * mps-flash-sdpa 0.1.0 ("Quick Start"); GQA, causal masking, the logsumexp that
+ * the forward caches and the backward consumes, and the two-kernel backward
+ * without atomics follow the MLX pull request "[Metal] Add Flash Attention VJP
+ * for training" ("Implementation Notes", "Key Features", "Limitations").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout      Row-major "BHLD", head dimension innermost, fully contiguous:
+ *               q, o, dO, dq : [B, Hq,  Lq,  D]
+ *               k, v, dk, dv : [B, Hkv, Lkv, D]
+ *               lse          : [B, Hq,  Lq]   float32, natural log
+ *             Query head h reads key/value head h / (Hq / Hkv).
+ * Masking     is_causal != 0 keeps key j for query i iff j <= i; it requires
+ *             Lq == Lkv. No other mask, no dropout.
+ * Precision   dtype is the operand type of q, k, v, dO (SDPA_F32, SDPA_F16 or
+ *             SDPA_BF16). Products accumulate in float32. out_dtype is the type
+ *             of o, dq, dk, dv and must be dtype or SDPA_F32 (with SDPA_F32
+ *             operands it must be SDPA_F32).
+ * Pointers    Device memory owned by the caller. Every tensor base must be
+ *             16-byte aligned. Outputs must not alias inputs or each other.
+ *             The library never allocates, frees, retains a pointer after the
+ *             call returns, or synchronises; work is enqueued on `stream`
+ *             (a hipStream_t; NULL means the default stream).
+ * Workspace   Caller-owned device scratch of at least sdpa_workspace_bytes(...)
+ *             bytes (may be NULL when that is 0), 256-byte aligned. Its contents
+ *             on entry do not matter. Calls that share a workspace must be
+ *             ordered on one stream.
+ * Errors      Arguments are validated before anything is enqueued. A failed
+ *             validation returns a non-zero status and touches no memory. A
+ *             launch failure returns SDPA_ERR_DEVICE. Faults inside a kernel
+ *             surface at the caller's next synchronisation, as for any stream
+ *             operation. All outputs are fully overwritten (dk and dv are not
+ *             accumulated into).
+ * Threads     No mutable global state; calls are thread-safe.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2 } sdpa_dtype_t;
+
+typedef enum {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  SDPA_ERR_SHAPE = 2,       /* a size < 1, Hq % Hkv != 0, or element counts overflow    */
+  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32, 64, 128}, causal with Lq != Lkv, bad dtype */
+  SDPA_ERR_WORKSPACE = 4,   /* workspace smaller than sdpa_workspace_bytes()            */
+  SDPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte (workspace: 256) aligned   */
+  SDPA_ERR_DEVICE = 6,      /* the HIP runtime rejected a launch                        */
+  SDPA_ERR_VALUE = 7        /* scale is not finite                                      */
+} sdpa_status_t;
+
+/* Kernel families, as returned by sdpa_select_path(). */
+enum {
+  SDPA_PATH_TILED = 0,  /* 16-bit operands, Lq > 8 or causal: MFMA tiles, online softmax  */
+  SDPA_PATH_VECTOR = 1, /* 16-bit, Lq <= 8, not causal, (Hq/Hkv)*Lq <= 32: keys split     */
+  SDPA_PATH_FP32 = 2    /* float32 operands                                               */
+};
+
+/*
+ * Which kernel family a call with these sizes runs (a pure host function).
+ * The short-query cutoff is the MLX pull request's vector VJP condition
+ * (L <= 8, "Implementation Notes"), read as the query length, non-causal, and
+ * limited to groups whose (Hq / Hkv) * Lq query rows fit one 32-row matrix block.
+ * Returns one of SDPA_PATH_*, or -1 if the combination is unsupported.
+ */
+int sdpa_select_path(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, int is_causal, sdpa_dtype_t dtype);
+
+/*
+ * Bytes of workspace sdpa_fwd (backward = 0) or sdpa_bwd (backward = 1) needs
+ * for these sizes; 0 if none. Pure host function. Returns (size_t)-1 when the
+ * sizes are invalid.
+ */
+size_t sdpa_workspace_bytes(int backward, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
+                            int64_t D, int is_causal, sdpa_dtype_t dtype);
+
+/*
+ * Forward: o = softmax((q k^T) * scale [+ causal]) v, and, when lse != NULL,
+ * lse[b, h, i] = log(sum_j exp(scale * q_i . k_j)) over the unmasked keys
+ * (the "second output" that the backward needs: MPS SDPA issue, section
+ * "Problem - Unused second output tensor"; pass NULL when no backward follows
+ * and it is not computed).
+ *
+ *   q, k, v    inputs in dtype (layouts above)
+ *   o          output in out_dtype, [B, Hq, Lq, D]
+ *   lse        optional output, float32 [B, Hq, Lq]
+ *   scale      multiplies the scores before the softmax (usually 1/sqrt(D))
+ */
+sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal,
+                       sdpa_dtype_t dtype, sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Backward of sdpa_fwd for the upstream gradient dO: writes dq, dk, dv (the
+ * gradients of sum(O * dO) with respect to q, k, v). `o` and `lse` must be
+ * exactly what sdpa_fwd wrote for the same q, k, v, scale and is_causal; lse is
+ * required (the MLX pull request, "Limitations": the VJP needs the forward's
+ * logsumexp). dk and dv sum the contributions of all query heads of a group.
+ *
+ *   q, k, v, dO   inputs in dtype;  o in out_dtype;  lse float32
+ *   dq, dk, dv    outputs in out_dtype
+ */
+sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
+                       int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. Never NULL. */
+const char* sdpa_status_str(sdpa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

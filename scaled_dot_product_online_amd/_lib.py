@@ -1,0 +1,163 @@
+"""ctypes binding of libsdpa_mi355x.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI declared
+in include/sdpa.h. This module turns torch tensors into device pointers, allocates
+outputs and the workspace with torch (device memory is plumbing here), passes
+torch's current HIP stream, and raises ``SdpaError`` on a non-zero status. There
+is no fallback: if the library is missing, loading it raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libsdpa_mi355x.so")
+
+F32, F16, BF16 = 0, 1, 2
+PATH_TILED, PATH_VECTOR, PATH_FP32 = 0, 1, 2
+PATH_NAMES = {PATH_TILED: "tiled", PATH_VECTOR: "vector", PATH_FP32: "fp32"}
+SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_status_str")
+
+_lib = None
+
+
+class SdpaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"sdpa status {status}: {msg}")
+        self.status = status
+
+
+def library():
+    """Load the shared library once (raises OSError/RuntimeError when it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m scaled_dot_product_online_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, c_int, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.sdpa_select_path.argtypes = [i64, i64, i64, i64, i64, c_int, c_int]
+    lib.sdpa_select_path.restype = c_int
+    lib.sdpa_workspace_bytes.argtypes = [c_int, i64, i64, i64, i64, i64, i64, c_int, c_int]
+    lib.sdpa_workspace_bytes.restype = ctypes.c_size_t
+    lib.sdpa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, c_int, c_int, c_int, vp,
+                             ctypes.c_size_t, vp]
+    lib.sdpa_fwd.restype = c_int
+    lib.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, c_int, c_int,
+                             c_int, vp, ctypes.c_size_t, vp]
+    lib.sdpa_bwd.restype = c_int
+    lib.sdpa_status_str.argtypes = [c_int]
+    lib.sdpa_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status):
+    return library().sdpa_status_str(int(status)).decode()
+
+
+def _check(status):
+    if status != 0:
+        raise SdpaError(status, status_str(status))
+
+
+def select_path(Hq, Hkv, Lq, Lkv, D, is_causal, dtype):
+    return library().sdpa_select_path(Hq, Hkv, Lq, Lkv, D, int(bool(is_causal)), dtype)
+
+
+def workspace_bytes(backward, B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype):
+    n = library().sdpa_workspace_bytes(int(bool(backward)), B, Hq, Hkv, Lq, Lkv, D, int(bool(is_causal)), dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise SdpaError(2, "invalid sizes")
+    return n
+
+
+# ---- torch-facing wrappers -------------------------------------------------------------
+
+def _torch_code(t):
+    import torch
+
+    codes = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t not in codes:
+        raise TypeError(f"unsupported dtype {t}")
+    return codes[t]
+
+
+def _torch_dtype(code):
+    import torch
+
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[code]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, L, D]")
+
+
+def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True, out=None, lse=None,
+             workspace=None, stream=None):
+    """O (and LSE when ``need_lse``) for BHLD tensors q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D]."""
+    import torch
+
+    _contig(q, k, v)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    dt = _torch_code(q.dtype)
+    odt = dt if out_dtype is None else _torch_code(out_dtype)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=_torch_dtype(odt), device=q.device)
+    if need_lse and lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if not need_lse:
+        lse = None
+    nws = workspace_bytes(0, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
+    if workspace is None and nws > 0:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    st = library().sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lkv, D, scale,
+                            int(bool(is_causal)), dt, odt, _ptr(workspace),
+                            workspace.numel() if workspace is not None else 0, _stream(q.device, stream))
+    _check(st)
+    return out, lse
+
+
+def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """dQ, dK, dV of sum(O * dO); ``o`` and ``lse`` are what sdpa_fwd returned."""
+    import torch
+
+    _contig(q, k, v, o, lse, dO)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    dt = _torch_code(q.dtype)
+    odt = dt if out_dtype is None else _torch_code(out_dtype)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    tdt = _torch_dtype(odt)
+    dq = torch.empty((B, Hq, Lq, D), dtype=tdt, device=q.device) if dq is None else dq
+    dk = torch.empty((B, Hkv, Lkv, D), dtype=tdt, device=q.device) if dk is None else dk
+    dv = torch.empty((B, Hkv, Lkv, D), dtype=tdt, device=q.device) if dv is None else dv
+    nws = workspace_bytes(1, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
+    st = library().sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+                            B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)), dt, odt, _ptr(workspace),
+                            workspace.numel(), _stream(q.device, stream))
+    _check(st)
+    return dq, dk, dv

@@ -1,0 +1,126 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used throughout (confirmed on gfx950 hardware with
+// integer-valued operands):
+//   v_mfma_f32_32x32x16_{bf16,f16}: lane l supplies row/column (l % 32) and the
+//   8 consecutive k values 8*(l/32) .. 8*(l/32)+7 of its A row / B column;
+//   accumulator element i of lane l is C[8*(i/4) + 4*(l/32) + (i%4)][l % 32].
+//   ds_read_b64_tr_b16: within each group of 16 lanes, lane L reads 4 16-bit
+//   elements at its own address; the result in lane i is element (i % 4) of
+//   the addresses given by lanes 4*r + i/4, r = 0..3 — i.e. when lanes 4r..4r+3
+//   address row r of a 4 x 16 block, lane i receives column i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Storage types. 16-bit operands travel as raw bits; the tag selects arithmetic.
+struct bf16_t { uint16_t bits; };
+struct f16_t { uint16_t bits; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- MFMA -------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c);
+template <> __device__ __forceinline__ f32x16_t mfma32<bf16_t>(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16_t mfma32<f16_t>(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+
+// ---- conversions --------------------------------------------------------------
+// Two fp32 values -> one dword of two 16-bit values (round to nearest even);
+// `lo` lands in bits 0..15.
+template <typename T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) {
+  bf16x2_t r = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float lo, float hi) {
+  f16x2_t r = __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+template <typename T> __device__ __forceinline__ float to_f32(uint16_t bits);
+template <> __device__ __forceinline__ float to_f32<bf16_t>(uint16_t bits) {
+  return __uint_as_float(((uint32_t)bits) << 16);
+}
+template <> __device__ __forceinline__ float to_f32<f16_t>(uint16_t bits) {
+  return (float)__builtin_bit_cast(_Float16, bits);
+}
+// Low / high 16-bit element of a dword as fp32.
+template <typename T> __device__ __forceinline__ float lo_f32(uint32_t w) { return to_f32<T>((uint16_t)(w & 0xffffu)); }
+template <typename T> __device__ __forceinline__ float hi_f32(uint32_t w) { return to_f32<T>((uint16_t)(w >> 16)); }
+
+// ---- exp2 / log2 (hardware v_exp_f32 / v_log_f32) --------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- half-wave exchange: lanes l and l^32 ------------------------------------------
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; feeding x twice leaves {own, partner} in each lane.
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- LDS -------------------------------------------------------------------------
+#define SDPA_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+
+// Transposed read of 4 16-bit elements (see the header comment), as two dwords.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+__device__ __forceinline__ u32x4_t lds_read16B(const uint16_t* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ void lds_write16B(uint16_t* p, u32x4_t v) { *(u32x4_t*)p = v; }
+
+// ---- global ------------------------------------------------------------------------
+__device__ __forceinline__ u32x4_t gload16B(const void* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ void gstore16B(void* p, u32x4_t v) { *(u32x4_t*)p = v; }
+__device__ __forceinline__ void gstore8B(void* p, u32x2_t v) { *(u32x2_t*)p = v; }
+
+// Store 4 consecutive fp32 results as OutT (16-bit tag types or float).
+template <typename OutT> struct Store4;
+template <> struct Store4<float> {
+  __device__ __forceinline__ static void run(float* p, float a, float b, float c, float d) {
+    *(f32x4_t*)p = (f32x4_t){a, b, c, d};
+  }
+};
+template <> struct Store4<bf16_t> {
+  __device__ __forceinline__ static void run(bf16_t* p, float a, float b, float c, float d) {
+    gstore8B(p, (u32x2_t){pack2<bf16_t>(a, b), pack2<bf16_t>(c, d)});
+  }
+};
+template <> struct Store4<f16_t> {
+  __device__ __forceinline__ static void run(f16_t* p, float a, float b, float c, float d) {
+    gstore8B(p, (u32x2_t){pack2<f16_t>(a, b), pack2<f16_t>(c, d)});
+  }
+};
+
+// Load one element of an output-typed array as fp32.
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const bf16_t* p) { return to_f32<bf16_t>(p->bits); }
+__device__ __forceinline__ float load_f32(const f16_t* p) { return to_f32<f16_t>(p->bits); }
+
+}  // namespace sdpa

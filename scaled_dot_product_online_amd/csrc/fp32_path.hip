@@ -1,0 +1,288 @@
+// float32 attention: forward, Delta pre-pass, dQ and dK/dV kernels on the vector ALUs.
+//
+// The float32 workloads on the pages are small (PyTensor issue "PERF: detect
+// scaled-dot-product-attention pattern ...", "Reproducer + metrics": B=8, H=8,
+// S=128, D=64) and their stated accuracy is 1e-5 ("Acceptance criteria"), so this
+// path keeps every product and sum in fp32 and runs on the VALUs: R = D/32 lanes
+// share one row, each holding a 32-element slice. It follows the same online
+// softmax (exp2 domain) and the same two-kernel backward without atomics as the
+// 16-bit path (MLX pull request "[Metal] Add Flash Attention VJP for training",
+// "Implementation Notes").
+#include "device_common.h"
+#include "kernels.h"
+
+namespace sdpa {
+namespace {
+
+constexpr int kF32Threads = 256;
+constexpr int kF32BN = 32;  // rows of the streamed operand per LDS tile
+
+template <int R>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < R; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// LDS tile of kF32BN rows: slice s of a row starts at s*33 so that the R lanes
+// of a row (reading different slices of the same row) hit different banks.
+template <int D>
+struct F32Tile {
+  static constexpr int R = D / 32;
+  static constexpr int PITCH = R * 33;
+  static constexpr int ELEMS = kF32BN * PITCH;
+  __device__ static int idx(int row, int d) { return row * PITCH + (d >> 5) * 33 + (d & 31); }
+  // Stage rows [r0, r0 + kF32BN) of a [L, D] matrix (rows >= L are zero).
+  __device__ static void stage(float* lds, const float* src, int r0, int L) {
+    for (int e = threadIdx.x; e < kF32BN * D; e += kF32Threads) {
+      const int r = e / D, d = e - r * D;
+      lds[idx(r, d)] = (r0 + r < L) ? src[(int64_t)(r0 + r) * D + d] : 0.f;
+    }
+  }
+};
+
+template <int D>
+__device__ __forceinline__ float dot_slice(const float* x, const float* lds, int row, int slice) {
+  const float* p = lds + row * F32Tile<D>::PITCH + slice * 33;
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc = fmaf(x[e], p[e], acc);
+  return acc;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                               const float* __restrict__ v, float* __restrict__ o,
+                                                               float* __restrict__ lse, int Hq, int G, int Lq,
+                                                               int Lkv, int n_qblk, float scale_log2) {
+  using TL = F32Tile<D>;
+  constexpr int R = TL::R, ROWS = kF32Threads / R;
+  __shared__ float k_lds[TL::ELEMS];
+  __shared__ float v_lds[TL::ELEMS];
+  const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
+  const int b = bh / Hq, hq = bh - b * Hq, Hkv = Hq / G, hk = hq / G;
+  const int slice = threadIdx.x % R, qrow = qblk * ROWS + threadIdx.x / R;
+  const float* kh = k + (int64_t)(b * Hkv + hk) * Lkv * D;
+  const float* vh = v + (int64_t)(b * Hkv + hk) * Lkv * D;
+  float qv[32], acc[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    qv[e] = (qrow < Lq) ? q[((int64_t)bh * Lq + qrow) * D + slice * 32 + e] : 0.f;
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS) : Lkv;
+  for (int t0 = 0; t0 < kv_end; t0 += kF32BN) {
+    __syncthreads();
+    TL::stage(k_lds, kh, t0, Lkv);
+    TL::stage(v_lds, vh, t0, Lkv);
+    __syncthreads();
+    float s[kF32BN];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kF32BN; ++j) {
+      float x = row_sum<R>(dot_slice<D>(qv, k_lds, j, slice)) * scale_log2;
+      const int key = t0 + j;
+      if (key >= Lkv || (CAUSAL && key > qrow)) x = -INFINITY;
+      s[j] = x;
+      tmax = fmaxf(tmax, x);
+    }
+    const float m_new = fmaxf(m, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kF32BN; ++j) {
+      const float p = fast_exp2(s[j] - m_use);
+      l += p;
+      const float* vr = v_lds + j * TL::PITCH + slice * 33;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc[e] = fmaf(p, vr[e], acc[e]);
+    }
+  }
+  if (qrow < Lq) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) o[((int64_t)bh * Lq + qrow) * D + slice * 32 + e] = acc[e] * inv;
+    if (lse != nullptr && slice == 0) lse[(int64_t)bh * Lq + qrow] = (m + fast_log2(l)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                              const float* __restrict__ v, const float* __restrict__ lse,
+                                                              const float* __restrict__ dO,
+                                                              const float* __restrict__ delta, float* __restrict__ dq,
+                                                              int Hq, int G, int Lq, int Lkv, int n_qblk,
+                                                              float scale_log2, float scale) {
+  using TL = F32Tile<D>;
+  constexpr int R = TL::R, ROWS = kF32Threads / R;
+  __shared__ float k_lds[TL::ELEMS];
+  __shared__ float v_lds[TL::ELEMS];
+  const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
+  const int b = bh / Hq, hq = bh - b * Hq, Hkv = Hq / G, hk = hq / G;
+  const int slice = threadIdx.x % R, qrow = qblk * ROWS + threadIdx.x / R;
+  const float* kh = k + (int64_t)(b * Hkv + hk) * Lkv * D;
+  const float* vh = v + (int64_t)(b * Hkv + hk) * Lkv * D;
+  const bool valid = qrow < Lq;
+  const int64_t roff = ((int64_t)bh * Lq + (valid ? qrow : 0)) * D + slice * 32;
+  float qv[32], dov[32], acc[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    qv[e] = valid ? q[roff + e] : 0.f;
+    dov[e] = valid ? dO[roff + e] : 0.f;
+    acc[e] = 0.f;
+  }
+  const float lse2 = valid ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
+  const float dlt = valid ? delta[(int64_t)bh * Lq + qrow] : 0.f;
+  const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS) : Lkv;
+  for (int t0 = 0; t0 < kv_end; t0 += kF32BN) {
+    __syncthreads();
+    TL::stage(k_lds, kh, t0, Lkv);
+    TL::stage(v_lds, vh, t0, Lkv);
+    __syncthreads();
+#pragma unroll 4
+    for (int j = 0; j < kF32BN; ++j) {
+      const float sv = row_sum<R>(dot_slice<D>(qv, k_lds, j, slice));
+      const float dp = row_sum<R>(dot_slice<D>(dov, v_lds, j, slice));
+      const int key = t0 + j;
+      float p = fast_exp2(fminf(sv * scale_log2 - lse2, 0.f));
+      if (key >= Lkv || (CAUSAL && key > qrow)) p = 0.f;
+      const float ds = p * (dp - dlt);
+      const float* kr = k_lds + j * TL::PITCH + slice * 33;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc[e] = fmaf(ds, kr[e], acc[e]);
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) dq[roff + e] = acc[e] * scale;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                               const float* __restrict__ v,
+                                                               const float* __restrict__ lse,
+                                                               const float* __restrict__ dO,
+                                                               const float* __restrict__ delta, float* __restrict__ dk,
+                                                               float* __restrict__ dv, int Hq, int G, int Lq, int Lkv,
+                                                               int n_kblk, float scale_log2, float scale) {
+  using TL = F32Tile<D>;
+  constexpr int R = TL::R, ROWS = kF32Threads / R;
+  __shared__ float q_lds[TL::ELEMS];
+  __shared__ float do_lds[TL::ELEMS];
+  __shared__ float lse_lds[kF32BN];
+  __shared__ float dl_lds[kF32BN];
+  const int bhk = blockIdx.x / n_kblk, kblk = blockIdx.x - bhk * n_kblk;
+  const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
+  const int slice = threadIdx.x % R, krow = kblk * ROWS + threadIdx.x / R;
+  const bool valid = krow < Lkv;
+  const int64_t roff = ((int64_t)bhk * Lkv + (valid ? krow : 0)) * D + slice * 32;
+  float kv_[32], vv[32], dka[32], dva[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    kv_[e] = valid ? k[roff + e] : 0.f;
+    vv[e] = valid ? v[roff + e] : 0.f;
+    dka[e] = 0.f;
+    dva[e] = 0.f;
+  }
+  // Causal: queries below the first key of this block never see it.
+  const int q_begin = CAUSAL ? (kblk * ROWS / kF32BN) * kF32BN : 0;
+  for (int gi = 0; gi < G; ++gi) {
+    const int hq = hk * G + gi;
+    const int64_t qbase = (int64_t)(b * Hq + hq) * Lq;
+    for (int t0 = q_begin; t0 < Lq; t0 += kF32BN) {
+      __syncthreads();
+      TL::stage(q_lds, q + qbase * D, t0, Lq);
+      TL::stage(do_lds, dO + qbase * D, t0, Lq);
+      if (threadIdx.x < kF32BN) {
+        const int i = t0 + threadIdx.x;
+        lse_lds[threadIdx.x] = (i < Lq) ? lse[qbase + i] * kLog2e : 0.f;
+        dl_lds[threadIdx.x] = (i < Lq) ? delta[qbase + i] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int j = 0; j < kF32BN; ++j) {
+        const int i = t0 + j;
+        const float sv = row_sum<R>(dot_slice<D>(kv_, q_lds, j, slice));
+        const float dp = row_sum<R>(dot_slice<D>(vv, do_lds, j, slice));
+        float p = fast_exp2(fminf(sv * scale_log2 - lse_lds[j], 0.f));
+        if (i >= Lq || (CAUSAL && krow > i)) p = 0.f;
+        const float ds = p * (dp - dl_lds[j]);
+        const float* qr = q_lds + j * TL::PITCH + slice * 33;
+        const float* dr = do_lds + j * TL::PITCH + slice * 33;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          dva[e] = fmaf(p, dr[e], dva[e]);
+          dka[e] = fmaf(ds, qr[e], dka[e]);
+        }
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      dk[roff + e] = dka[e] * scale;
+      dv[roff + e] = dva[e];
+    }
+  }
+}
+
+template <int D, bool C>
+hipError_t fwd_typed(const Shape& s, const float* q, const float* k, const float* v, float* o, float* lse, float scale,
+                     hipStream_t st) {
+  constexpr int ROWS = kF32Threads / (D / 32);
+  const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, o, lse,
+                     (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk,
+                     (float)((double)scale * 1.4426950408889634));
+  return hipGetLastError();
+}
+
+template <int D, bool C>
+hipError_t bwd_typed(const Shape& s, const float* q, const float* k, const float* v, const float* lse,
+                     const float* dO, const float* delta, float* dq, float* dk, float* dv, float scale,
+                     hipStream_t st) {
+  constexpr int ROWS = kF32Threads / (D / 32);
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
+  hipLaunchKernelGGL((dq_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
+                     delta, dq, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, scale_log2, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_kblk = (int)((s.Lkv + ROWS - 1) / ROWS);
+  hipLaunchKernelGGL((dkv_f32_kernel<D, C>), dim3(n_kblk * s.B * s.Hkv), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
+                     delta, dk, dv, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_kblk, scale_log2, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v, float* o,
+                          float* lse, float scale, hipStream_t st) {
+  switch (s.D) {
+    case 32: return causal ? fwd_typed<32, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<32, false>(s, q, k, v, o, lse, scale, st);
+    case 64: return causal ? fwd_typed<64, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<64, false>(s, q, k, v, o, lse, scale, st);
+    case 128: return causal ? fwd_typed<128, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<128, false>(s, q, k, v, o, lse, scale, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v,
+                          const float* o, const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                          float* delta, float scale, hipStream_t st) {
+  hipError_t e = launch_delta(s, kF32, kF32, o, dO, delta, st);
+  if (e != hipSuccess) return e;
+  switch (s.D) {
+    case 32: return causal ? bwd_typed<32, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st) : bwd_typed<32, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st);
+    case 64: return causal ? bwd_typed<64, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st) : bwd_typed<64, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st);
+    case 128: return causal ? bwd_typed<128, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st) : bwd_typed<128, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sdpa

@@ -1,0 +1,47 @@
+// Internal launch interface between the C-ABI layer (sdpa_api.hip) and the
+// kernel translation units. Shapes are validated by the caller; every launcher
+// returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+enum Dt { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct Shape {
+  int64_t B, Hq, Hkv, Lq, Lkv, D;
+};
+
+// Delta_i = sum_d dO[i,d] * O[i,d] over all B*Hq*Lq rows (delta.hip).
+hipError_t launch_delta(const Shape& s, Dt o_dt, Dt do_dt, const void* o, const void* dO, float* delta,
+                        hipStream_t st);
+
+// Tiled forward, 16-bit operands (fwd_tiled.hip).
+hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
+                            void* o, float* lse, float scale, hipStream_t st);
+
+// Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is [B*Hq*Lq] fp32 scratch.
+hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                            float* delta, float scale, hipStream_t st);
+
+// float32 path (fp32_path.hip).
+hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v, float* o,
+                          float* lse, float scale, hipStream_t st);
+hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v,
+                          const float* o, const float* lse, const float* dO, float* dq, float* dk, float* dv,
+                          float* delta, float scale, hipStream_t st);
+
+// Short-query path (vector_path.hip).
+int vector_num_splits(const Shape& s);
+size_t vector_fwd_workspace(const Shape& s);
+size_t vector_bwd_workspace(const Shape& s);
+hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v, void* o,
+                             float* lse, float scale, void* ws, hipStream_t st);
+hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
+                             float scale, hipStream_t st);
+
+}  // namespace sdpa

@@ -1,0 +1,586 @@
+// Short-query attention (Lq <= 8, not causal) for 16-bit operands on gfx950.
+//
+// The MLX pull request "[Metal] Add Flash Attention VJP for training"
+// ("Implementation Notes", vector VJP for L <= 8, fp32 accumulators) treats short
+// queries separately: the work is one pass over K and V, so the kernels are sized
+// for HBM bandwidth, not for the matrix cores. Here the G*Lq (<= 32) query rows of
+// a GQA group are packed into the 32 rows of one MFMA block (they are contiguous
+// in BHLD memory: head hk*G + r/Lq, query r%Lq is row hk*G*Lq + r), and the keys
+// of each (b, hk) are split across workgroups so that the few groups still fill
+// the chip.
+//
+// Forward:  vec_fwd_kernel  — split s, wave w streams its own contiguous segment of
+//                            the split in 32-key tiles with an online softmax;
+//                            the 4 waves merge in LDS; the split writes
+//                            (O_unnormalised, m, l) partials, or the final O and
+//                            logsumexp when there is one split.
+//           vec_combine_kernel — merges the splits' partials per row:
+//                            m* = max m_s, l* = sum l_s 2^(m_s-m*),
+//                            O = sum O_s 2^(m_s-m*) / l*, LSE = (m* + log2 l*) ln 2.
+// Backward: vec_bwd_kernel  — split s, wave w owns 32 keys per step exclusively:
+//                            P from the logsumexp, dP, dS; dV = P^T dO and
+//                            dK = scale dS^T Q are complete for those keys (all
+//                            query rows of the group are resident) and are stored
+//                            directly; dS is also transposed through LDS into
+//                            dQ^T += K^T dS^T, summed over the split's keys.
+//           vec_dq_reduce_kernel — dQ = scale * sum_s dQ_s.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace sdpa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTileKeys = 32;            // keys per wave per step
+constexpr int kStepKeys = kWaves * kTileKeys;
+constexpr int kTargetBlocks = 1024;      // ~4 workgroups per CU on 256 CUs
+
+struct SplitPlan {
+  int nsplit;
+  int64_t split_len;  // keys per split, a multiple of kStepKeys
+};
+
+SplitPlan plan(const Shape& s) {
+  const int64_t groups = s.B * s.Hkv;
+  const int64_t steps = (s.Lkv + kStepKeys - 1) / kStepKeys;
+  int64_t want = (kTargetBlocks + groups - 1) / groups;
+  if (want < 1) want = 1;
+  if (want > steps) want = steps;
+  const int64_t len = ((s.Lkv + want - 1) / want + kStepKeys - 1) / kStepKeys * kStepKeys;
+  return SplitPlan{(int)((s.Lkv + len - 1) / len), len};
+}
+
+int64_t rows_total(const Shape& s) { return s.B * s.Hq * s.Lq; }
+
+template <int D>
+struct VecTile {
+  static constexpr int P = D + 8;           // K/V/Q/dO tile row pitch (elements)
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int LPW = 64 / CPR;      // rows per wave-wide load
+  static constexpr int LOADS = kTileKeys / LPW;
+  static constexpr int DSP = 32 + 16;       // dS^T scratch pitch
+};
+
+// Load rows [r0, r0+32) x D of a row-major [.., D] matrix (rows >= rmax are zero),
+// one 16-byte chunk per lane per load; consecutive lanes read consecutive chunks.
+template <int D>
+__device__ __forceinline__ void wave_fetch(u32x4_t* buf, const uint16_t* base, int64_t r0, int64_t rmax, int lane) {
+  using TL = VecTile<D>;
+#pragma unroll
+  for (int p = 0; p < TL::LOADS; ++p) {
+    const int r = p * TL::LPW + lane / TL::CPR;
+    const int c = (lane % TL::CPR) * 8;
+    buf[p] = (r0 + r < rmax) ? gload16B(base + (r0 + r) * D + c) : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+}
+template <int D>
+__device__ __forceinline__ void wave_store(uint16_t* lds, const u32x4_t* buf, int lane) {
+  using TL = VecTile<D>;
+#pragma unroll
+  for (int p = 0; p < TL::LOADS; ++p) {
+    const int r = p * TL::LPW + lane / TL::CPR;
+    const int c = (lane % TL::CPR) * 8;
+    lds_write16B(lds + r * TL::P + c, buf[p]);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Forward split
+// ---------------------------------------------------------------------------------
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void vec_fwd_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v, OutT* __restrict__ o,
+                                                              float* __restrict__ lse, float* __restrict__ part_o,
+                                                              float* __restrict__ part_ml, int Hq, int G, int Lq,
+                                                              int Lkv, int nsplit, int split_len, int n_rb,
+                                                              int64_t total_rows, float scale_log2) {
+  using TL = VecTile<D>;
+  constexpr int WAVE_LDS = 2 * kTileKeys * TL::P;  // K and V tile of one wave
+  static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS * 2, "merge scratch must fit in the tile LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * WAVE_LDS];
+  __shared__ float mrg_m[kWaves][32];
+  __shared__ float mrg_l[kWaves][32];
+
+  const int split = blockIdx.x % nsplit;
+  const int rb = (blockIdx.x / nsplit) % n_rb;
+  const int bhk = blockIdx.x / (nsplit * n_rb);
+  const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, g = lane >> 5;
+  const int rows = G * Lq;
+  const int r = rb * 32 + n;  // packed row of this lane
+  const bool row_ok = r < rows;
+  const int64_t row0 = (int64_t)b * Hq * Lq + (int64_t)hk * G * Lq;  // first packed row of the group
+  const int64_t kv0 = (int64_t)bhk * Lkv;
+
+  u32x4_t qop[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c)
+    qop[c] = row_ok ? gload16B(q + (row0 + r) * D + 16 * c + 8 * g) : (u32x4_t){0u, 0u, 0u, 0u};
+
+  // This wave's contiguous key segment.
+  const int seg = split_len / kWaves;
+  const int kb0 = split * split_len + wave * seg;
+  const int kb1 = min(kb0 + seg, Lkv);
+  const int steps = seg / kTileKeys;
+
+  uint16_t* k_lds = lds + wave * WAVE_LDS;
+  uint16_t* v_lds = k_lds + kTileKeys * TL::P;
+  f32x16_t oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+  u32x4_t kbuf[TL::LOADS], vbuf[TL::LOADS];
+  wave_fetch<D>(kbuf, k + kv0 * D, kb0, kb1, lane);
+  wave_fetch<D>(vbuf, v + kv0 * D, kb0, kb1, lane);
+  const int G16 = lane >> 4, L16 = lane & 15;
+  for (int st = 0; st < steps; ++st) {
+    __syncthreads();  // every wave has finished reading its previous tile
+    wave_store<D>(k_lds, kbuf, lane);
+    wave_store<D>(v_lds, vbuf, lane);
+    __syncthreads();
+    const int t0 = kb0 + st * kTileKeys;
+    if (st + 1 < steps) {
+      wave_fetch<D>(kbuf, k + kv0 * D, t0 + kTileKeys, kb1, lane);
+      wave_fetch<D>(vbuf, v + kv0 * D, t0 + kTileKeys, kb1, lane);
+    }
+    if (t0 >= kb1) continue;  // ragged tail: nothing left in this wave's segment
+    f32x16_t s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) s = mfma32<T>(lds_read16B(k_lds + n * TL::P + 16 * c + 8 * g), qop[c], s);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float x = s[i] * scale_log2;
+      if (t0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kb1) x = -INFINITY;
+      s[i] = x;
+      tmax = fmaxf(tmax, x);
+    }
+    tmax = half_swap_max(tmax);
+    const float m_new = fmaxf(m, tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    lsum *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    u32x4_t pop[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(s[8 * c2 + e] - m_use);
+        lsum += p[e];
+      }
+      pop[c2] = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]), pack2<T>(p[6], p[7])};
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int row = 16 * c2 + 4 * g + (L16 >> 2);
+        const u32x2_t lo = lds_read_tr16(v_lds + row * TL::P + col);
+        const u32x2_t hi = lds_read_tr16(v_lds + (row + 8) * TL::P + col);
+        oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop[c2], oacc[db]);
+      }
+    }
+  }
+  const float l = half_swap_sum(lsum);
+
+  // Merge the 4 waves: scratch O_w (fp32, [32 rows][D]) reuses the tile LDS.
+  __syncthreads();
+  float* mrg_o = (float*)lds;  // kWaves * 32 * D floats <= kWaves * WAVE_LDS * 2 bytes
+  if (g == 0) {
+    mrg_m[wave][n] = m;
+    mrg_l[wave][n] = l;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *(f32x4_t*)(mrg_o + (wave * 32 + n) * D + db * 32 + 8 * r4 + 4 * g) =
+          (f32x4_t){oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]};
+  __syncthreads();
+  // 256 threads: row = tid / 8, 8 threads per row, D/8 columns each.
+  const int mr = tid >> 3, part = tid & 7;
+  const int rr = rb * 32 + mr;
+  float mw[kWaves], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = mrg_m[w][mr];
+    M = fmaxf(M, mw[w]);
+  }
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float sc[kWaves], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    sc[w] = fast_exp2(mw[w] - Mu);
+    L += mrg_l[w][mr] * sc[w];
+  }
+  if (rr < rows) {
+    const int64_t grow = row0 + rr;
+    if (nsplit == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      for (int d = part * 4; d < D; d += 32) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float a = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) a += mrg_o[(w * 32 + mr) * D + d + j] * sc[w];
+          x[j] = a * inv;
+        }
+        Store4<OutT>::run(o + grow * D + d, x[0], x[1], x[2], x[3]);
+      }
+      if (lse != nullptr && part == 0) lse[grow] = (M + fast_log2(L)) * kLn2;
+    } else {
+      float* pod = part_o + ((int64_t)split * total_rows + grow) * D;  // [split][row][D]
+      for (int d = part * 4; d < D; d += 32) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float a = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) a += mrg_o[(w * 32 + mr) * D + d + j] * sc[w];
+          x[j] = a;
+        }
+        *(f32x4_t*)(pod + d) = (f32x4_t){x[0], x[1], x[2], x[3]};
+      }
+      if (part == 0) {
+        part_ml[((int64_t)split * total_rows + grow) * 2 + 0] = M;
+        part_ml[((int64_t)split * total_rows + grow) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __restrict__ part_o,
+                                                               const float* __restrict__ part_ml,
+                                                               OutT* __restrict__ o, float* __restrict__ lse,
+                                                               int64_t total_rows, int nsplit) {
+  constexpr int TPR = D / 4;  // threads per row, 4 columns each
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 4;
+  if (row >= total_rows) return;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((int64_t)s * total_rows + row) * 2]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f, x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const int64_t pr = (int64_t)s * total_rows + row;
+    const float w = fast_exp2(part_ml[pr * 2] - Mu);
+    L += part_ml[pr * 2 + 1] * w;
+    const f32x4_t a = *(const f32x4_t*)(part_o + pr * D + c);
+    x0 += a[0] * w;
+    x1 += a[1] * w;
+    x2 += a[2] * w;
+    x3 += a[3] * w;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  Store4<OutT>::run(o + row * D + c, x0 * inv, x1 * inv, x2 * inv, x3 * inv);
+  if (lse != nullptr && c == 0) lse[row] = (M + fast_log2(L)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------------
+// Backward split
+// ---------------------------------------------------------------------------------
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __restrict__ q,
+                                                              const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v,
+                                                              const OutT* __restrict__ o,
+                                                              const float* __restrict__ lse,
+                                                              const uint16_t* __restrict__ dO, OutT* __restrict__ dk,
+                                                              OutT* __restrict__ dv, float* __restrict__ dq_part,
+                                                              int Hq, int G, int Lq, int Lkv, int nsplit,
+                                                              int split_len, int64_t total_rows, float scale_log2,
+                                                              float scale) {
+  using TL = VecTile<D>;
+  constexpr int WAVE_LDS = 2 * kTileKeys * TL::P + kTileKeys * TL::DSP;
+  static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS * 2, "dQ reduction scratch must fit in the tile LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * WAVE_LDS];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[32 * TL::P];
+  __shared__ __attribute__((aligned(16))) uint16_t do_lds[32 * TL::P];
+  __shared__ __attribute__((aligned(16))) float lse_lds[32];
+  __shared__ __attribute__((aligned(16))) float dl_lds[32];
+
+  const int split = blockIdx.x % nsplit;
+  const int bhk = blockIdx.x / nsplit;
+  const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, g = lane >> 5;
+  const int rows = G * Lq;
+  const int64_t row0 = (int64_t)b * Hq * Lq + (int64_t)hk * G * Lq;
+  const int64_t kv0 = (int64_t)bhk * Lkv;
+
+  // Stage Q and dO of the group's rows; Delta and LSE*log2e per row.
+  {
+    constexpr int CPR = D / 8;
+    for (int e = tid; e < 32 * CPR; e += kThreads) {
+      const int r = e / CPR, c = (e % CPR) * 8;
+      const bool ok = r < rows;
+      lds_write16B(q_lds + r * TL::P + c, ok ? gload16B(q + (row0 + r) * D + c) : (u32x4_t){0u, 0u, 0u, 0u});
+      lds_write16B(do_lds + r * TL::P + c, ok ? gload16B(dO + (row0 + r) * D + c) : (u32x4_t){0u, 0u, 0u, 0u});
+    }
+    // Delta: 8 threads per row.
+    const int r = tid >> 3, part = tid & 7;
+    float acc = 0.f;
+    if (r < rows) {
+      for (int d = part; d < D; d += 8) acc = fmaf(load_f32(o + (row0 + r) * D + d), to_f32<T>(dO[(row0 + r) * D + d]), acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    if (part == 0) {
+      dl_lds[r] = acc;
+      lse_lds[r] = (r < rows) ? lse[row0 + r] * kLog2e : 0.f;
+    }
+  }
+
+  const int seg = split_len / kWaves;
+  const int kb0 = split * split_len + wave * seg;
+  const int kb1 = min(kb0 + seg, Lkv);
+  const int steps = seg / kTileKeys;
+  uint16_t* k_lds = lds + wave * WAVE_LDS;
+  uint16_t* v_lds = k_lds + kTileKeys * TL::P;
+  uint16_t* ds_lds = v_lds + kTileKeys * TL::P;
+
+  f32x16_t dqa[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
+  u32x4_t kbuf[TL::LOADS], vbuf[TL::LOADS];
+  wave_fetch<D>(kbuf, k + kv0 * D, kb0, kb1, lane);
+  wave_fetch<D>(vbuf, v + kv0 * D, kb0, kb1, lane);
+  const int G16 = lane >> 4, L16 = lane & 15;
+  for (int st = 0; st < steps; ++st) {
+    __syncthreads();
+    wave_store<D>(k_lds, kbuf, lane);
+    wave_store<D>(v_lds, vbuf, lane);
+    __syncthreads();
+    const int t0 = kb0 + st * kTileKeys;
+    if (st + 1 < steps) {
+      wave_fetch<D>(kbuf, k + kv0 * D, t0 + kTileKeys, kb1, lane);
+      wave_fetch<D>(vbuf, v + kv0 * D, t0 + kTileKeys, kb1, lane);
+    }
+    if (t0 >= kb1) continue;
+    const int key = t0 + n;  // this lane's key column
+    // S = Q K^T and dP = dO V^T: rows = query rows, columns = this wave's 32 keys.
+    f32x16_t s, dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = 0.f;
+      dp[i] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s = mfma32<T>(lds_read16B(q_lds + n * TL::P + 16 * c + 8 * g), lds_read16B(k_lds + n * TL::P + 16 * c + 8 * g), s);
+      dp = mfma32<T>(lds_read16B(do_lds + n * TL::P + 16 * c + 8 * g), lds_read16B(v_lds + n * TL::P + 16 * c + 8 * g), dp);
+    }
+    u32x4_t pop[2], dsop[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r0 = 16 * c2 + 8 * h + 4 * g;
+        const f32x4_t l4 = *(const f32x4_t*)(lse_lds + r0);
+        const f32x4_t d4 = *(const f32x4_t*)(dl_lds + r0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 8 * c2 + 4 * h + j;
+          float p = fast_exp2(fminf(s[i] * scale_log2 - l4[j], 0.f));
+          if (r0 + j >= rows || key >= kb1) p = 0.f;
+          pv[4 * h + j] = p;
+          dsv[4 * h + j] = p * (dp[i] - d4[j]);
+        }
+      }
+      pop[c2] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]), pack2<T>(pv[6], pv[7])};
+      dsop[c2] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
+                           pack2<T>(dsv[6], dsv[7])};
+      // dS^T scratch, row = key n, columns = query rows (4 consecutive rows per dword pair).
+      *(u32x2_t*)(ds_lds + n * TL::DSP + 16 * c2 + 4 * g) = (u32x2_t){dsop[c2][0], dsop[c2][1]};
+      *(u32x2_t*)(ds_lds + n * TL::DSP + 16 * c2 + 8 + 4 * g) = (u32x2_t){dsop[c2][2], dsop[c2][3]};
+    }
+    // dV^T = dO^T P and dK^T = Q^T dS for this wave's keys (complete: all rows are here).
+    f32x16_t dva[D / 32], dka[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dva[db][i] = 0.f;
+        dka[db][i] = 0.f;
+      }
+      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int row = 16 * c2 + 4 * g + (L16 >> 2);
+        const u32x2_t dlo = lds_read_tr16(do_lds + row * TL::P + col), dhi = lds_read_tr16(do_lds + (row + 8) * TL::P + col);
+        dva[db] = mfma32<T>((u32x4_t){dlo[0], dlo[1], dhi[0], dhi[1]}, pop[c2], dva[db]);
+        const u32x2_t qlo = lds_read_tr16(q_lds + row * TL::P + col), qhi = lds_read_tr16(q_lds + (row + 8) * TL::P + col);
+        dka[db] = mfma32<T>((u32x4_t){qlo[0], qlo[1], qhi[0], qhi[1]}, dsop[c2], dka[db]);
+      }
+    }
+    if (key < kb1) {
+      const int64_t kro = (kv0 + key) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * g;
+          Store4<OutT>::run(dk + kro + d, dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale,
+                            dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale);
+          Store4<OutT>::run(dv + kro + d, dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2], dva[db][4 * r4 + 3]);
+        }
+    }
+    // dQ^T += K^T dS^T over this wave's 32 keys: chunk c2 = keys 16*c2 + 8g' .. +7.
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int krow = 16 * c2 + 8 * g + (L16 >> 2);
+      const u32x2_t blo = lds_read_tr16(ds_lds + krow * TL::DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
+      const u32x2_t bhi = lds_read_tr16(ds_lds + (krow + 4) * TL::DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
+      const u32x4_t bop = (u32x4_t){blo[0], blo[1], bhi[0], bhi[1]};
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
+        const u32x2_t alo = lds_read_tr16(k_lds + krow * TL::P + col);
+        const u32x2_t ahi = lds_read_tr16(k_lds + (krow + 4) * TL::P + col);
+        dqa[db] = mfma32<T>((u32x4_t){alo[0], alo[1], ahi[0], ahi[1]}, bop, dqa[db]);
+      }
+    }
+  }
+  // Sum the 4 waves' dQ^T (lane (n, g) holds row n, d = db*32 + 8*(i/4) + 4g + i%4).
+  __syncthreads();
+  float* red = (float*)lds;  // kWaves * 32 * D floats
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *(f32x4_t*)(red + (wave * 32 + n) * D + db * 32 + 8 * r4 + 4 * g) =
+          (f32x4_t){dqa[db][4 * r4], dqa[db][4 * r4 + 1], dqa[db][4 * r4 + 2], dqa[db][4 * r4 + 3]};
+  __syncthreads();
+  for (int e = tid; e < 32 * (D / 4); e += kThreads) {
+    const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+    if (r >= rows) continue;
+    f32x4_t a = *(const f32x4_t*)(red + r * D + c);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f32x4_t x = *(const f32x4_t*)(red + (w * 32 + r) * D + c);
+      a[0] += x[0];
+      a[1] += x[1];
+      a[2] += x[2];
+      a[3] += x[3];
+    }
+    *(f32x4_t*)(dq_part + ((int64_t)split * total_rows + row0 + r) * D + c) = a;
+  }
+}
+
+template <int D, typename OutT>
+__global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __restrict__ dq_part,
+                                                                 OutT* __restrict__ dq, int64_t total_rows,
+                                                                 int nsplit, float scale) {
+  const int64_t e4 = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // one group of 4 columns
+  if (e4 >= total_rows * (D / 4)) return;
+  float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const f32x4_t a = *(const f32x4_t*)(dq_part + (int64_t)s * total_rows * D + e4 * 4);
+    x0 += a[0];
+    x1 += a[1];
+    x2 += a[2];
+    x3 += a[3];
+  }
+  Store4<OutT>::run(dq + e4 * 4, x0 * scale, x1 * scale, x2 * scale, x3 * scale);
+}
+
+template <typename T, int D, typename OutT>
+hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse, float scale,
+                     void* ws, hipStream_t st) {
+  const SplitPlan pl = plan(s);
+  const int G = (int)(s.Hq / s.Hkv);
+  const int n_rb = (int)((G * s.Lq + 31) / 32);
+  const int64_t tr = rows_total(s);
+  float* part_o = (float*)ws;
+  float* part_ml = part_o + (int64_t)pl.nsplit * tr * D;
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipLaunchKernelGGL((vec_fwd_kernel<T, D, OutT>), dim3(pl.nsplit * n_rb * s.B * s.Hkv), dim3(kThreads), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, part_o, part_ml,
+                     (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nsplit == 1) return e;
+  constexpr int RPB = kThreads / (D / 4);
+  hipLaunchKernelGGL((vec_combine_kernel<D, OutT>), dim3((unsigned)((tr + RPB - 1) / RPB)), dim3(kThreads), 0, st,
+                     (const float*)part_o, (const float*)part_ml, (OutT*)o, lse, tr, pl.nsplit);
+  return hipGetLastError();
+}
+
+template <typename T, int D, typename OutT>
+hipError_t bwd_typed(const Shape& s, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv, void* ws, float scale, hipStream_t st) {
+  const SplitPlan pl = plan(s);
+  const int G = (int)(s.Hq / s.Hkv);
+  const int64_t tr = rows_total(s);
+  float* dq_part = (float*)ws;
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634);
+  hipLaunchKernelGGL((vec_bwd_kernel<T, D, OutT>), dim3(pl.nsplit * s.B * s.Hkv), dim3(kThreads), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
+                     (const uint16_t*)dO, (OutT*)dk, (OutT*)dv, dq_part, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv,
+                     pl.nsplit, (int)pl.split_len, tr, scale_log2, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n4 = tr * (D / 4);
+  hipLaunchKernelGGL((vec_dq_reduce_kernel<D, OutT>), dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, st, (const float*)dq_part, (OutT*)dq, tr, pl.nsplit, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int vector_num_splits(const Shape& s) { return plan(s).nsplit; }
+
+size_t vector_fwd_workspace(const Shape& s) {
+  const SplitPlan pl = plan(s);
+  if (pl.nsplit == 1) return 0;
+  return (size_t)pl.nsplit * (size_t)rows_total(s) * (size_t)(s.D + 2) * sizeof(float);
+}
+
+size_t vector_bwd_workspace(const Shape& s) {
+  return (size_t)plan(s).nsplit * (size_t)rows_total(s) * (size_t)s.D * sizeof(float);
+}
+
+#define SDPA_VEC_DISPATCH(FN, ...)                                                                          \
+  switch (s.D) {                                                                                            \
+    case 32: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 32, float>(__VA_ARGS__) : FN<bf16_t, 32, bf16_t>(__VA_ARGS__)) \
+                                : (out == kF32 ? FN<f16_t, 32, float>(__VA_ARGS__) : FN<f16_t, 32, f16_t>(__VA_ARGS__));   \
+    case 64: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 64, float>(__VA_ARGS__) : FN<bf16_t, 64, bf16_t>(__VA_ARGS__)) \
+                                : (out == kF32 ? FN<f16_t, 64, float>(__VA_ARGS__) : FN<f16_t, 64, f16_t>(__VA_ARGS__));   \
+    case 128: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 128, float>(__VA_ARGS__) : FN<bf16_t, 128, bf16_t>(__VA_ARGS__)) \
+                                 : (out == kF32 ? FN<f16_t, 128, float>(__VA_ARGS__) : FN<f16_t, 128, f16_t>(__VA_ARGS__));   \
+    default: return hipErrorInvalidValue;                                                                   \
+  }
+
+hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v, void* o,
+                             float* lse, float scale, void* ws, hipStream_t st) {
+  if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
+  SDPA_VEC_DISPATCH(fwd_typed, s, q, k, v, o, lse, scale, ws, st)
+}
+
+hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
+                             float scale, hipStream_t st) {
+  if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
+  SDPA_VEC_DISPATCH(bwd_typed, s, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, st)
+}
+
+}  // namespace sdpa

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/sdpa.h declares, and rejects bad arguments before touching memory."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_dot_product_online_amd as sd
+from scaled_dot_product_online_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "sdpa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdpa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sd.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(8):
+        assert sd.status_str(code)
+    assert sd.status_str(99) == "unknown status"
+
+
+def test_select_path():
+    assert sd.select_path(32, 4, 4096, 4096, 128, True, sd.BF16) == sd.PATH_TILED
+    assert sd.select_path(32, 8, 8, 8192, 128, False, sd.BF16) == sd.PATH_VECTOR
+    assert sd.select_path(32, 8, 1, 8192, 64, False, sd.F16) == sd.PATH_VECTOR
+    assert sd.select_path(32, 8, 8, 8, 64, True, sd.F16) == sd.PATH_TILED      # causal never takes the vector path
+    assert sd.select_path(32, 8, 9, 8192, 64, False, sd.F16) == sd.PATH_TILED
+    assert sd.select_path(64, 4, 8, 8192, 64, False, sd.F16) == sd.PATH_TILED  # 16*8 rows exceed one block
+    assert sd.select_path(8, 8, 128, 128, 64, False, sd.F32) == sd.PATH_FP32
+    assert sd.select_path(8, 8, 128, 128, 96, False, sd.F16) == -1           # unsupported head dim
+    assert sd.select_path(8, 8, 128, 64, 64, True, sd.F16) == -1             # causal needs Lq == Lkv
+    assert sd.select_path(8, 3, 128, 128, 64, False, sd.F16) == -1           # Hq % Hkv
+
+
+def test_workspace_sizes():
+    # tiled and fp32 forward need none; backward keeps Delta (fp32 per query row)
+    assert sd.workspace_bytes(0, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) == 0
+    assert sd.workspace_bytes(1, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) >= 4 * 32 * 4096 * 4
+    assert sd.workspace_bytes(1, 8, 8, 8, 128, 128, 64, False, sd.F32) >= 8 * 8 * 128 * 4
+    # vector path: split partials
+    assert sd.workspace_bytes(0, 16, 32, 8, 8, 8192, 128, False, sd.BF16) > 0
+    assert sd.workspace_bytes(1, 16, 32, 8, 8, 8192, 128, False, sd.BF16) >= 16 * 32 * 8 * 128 * 4
+    with pytest.raises(sd.SdpaError):
+        sd.workspace_bytes(0, 0, 1, 1, 1, 1, 64, False, sd.F16)
+
+
+def _no_device():
+    """The validation tests pass fake, never-dereferenced pointers; they only run where no
+    GPU is visible, so that a validation slip cannot turn into a launch on real memory."""
+    from conftest import gpu_available
+
+    if gpu_available():
+        pytest.skip("fake-pointer validation tests run only without a GPU")
+
+
+def _fwd(lib, q=1, k=1, v=1, o=1, lse=0, B=1, Hq=1, Hkv=1, Lq=16, Lkv=16, D=64, scale=0.125, causal=0, dt=1,
+         odt=1, ws=0, wsb=0):
+    p = lambda x: ctypes.c_void_p(x * 256 if x else 0)  # noqa: E731  (aligned fake addresses, never dereferenced)
+    return lib.sdpa_fwd(p(q), p(k), p(v), p(o), p(lse), B, Hq, Hkv, Lq, Lkv, D, scale, causal, dt, odt, p(ws), wsb,
+                        None)
+
+
+def test_forward_validation_rejects_before_launch():
+    _no_device()
+    lib = sd.library()
+    assert _fwd(lib, q=0) == 1                        # NULL
+    assert _fwd(lib, B=0) == 2                        # shape
+    assert _fwd(lib, Hq=3, Hkv=2) == 2                # Hq % Hkv
+    assert _fwd(lib, D=96) == 3                       # head dim
+    assert _fwd(lib, Lq=16, Lkv=32, causal=1) == 3    # causal needs Lq == Lkv
+    assert _fwd(lib, dt=1, odt=2) == 3                # out dtype must be dtype or f32
+    assert _fwd(lib, dt=0, odt=1) == 3                # f32 operands need f32 outputs
+    assert _fwd(lib, dt=5) == 3
+    assert _fwd(lib, scale=float("inf")) == 7
+    assert _fwd(lib, scale=float("nan")) == 7
+    assert _fwd(lib, B=1 << 40, Hq=1 << 20) == 2      # overflow
+    assert _fwd(lib, Lq=4, Lkv=8192, Hq=8, Hkv=2) == 4  # vector path needs its workspace
+    misaligned = lib.sdpa_fwd(ctypes.c_void_p(258), ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                              None, 1, 1, 1, 16, 16, 64, 0.125, 0, 1, 1, None, 0, None)
+    assert misaligned == 5
+
+
+def test_backward_requires_lse_and_workspace():
+    _no_device()
+    lib = sd.library()
+    p = lambda x: ctypes.c_void_p(x * 256 if x else 0)  # noqa: E731
+    args = [p(1), p(1), p(1), p(1), p(0), p(1), p(1), p(1), p(1), 1, 1, 1, 16, 16, 64, 0.125, 0, 1, 1, p(1), 1 << 20,
+            None]
+    assert lib.sdpa_bwd(*args) == 1                    # lse is required
+    args[4] = p(1)
+    args[19], args[20] = p(0), 0
+    assert lib.sdpa_bwd(*args) == 4                    # workspace required
+    args[19], args[20] = ctypes.c_void_p(256 + 16), 1 << 20
+    assert lib.sdpa_bwd(*args) == 5                    # workspace alignment
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.library()

@@ -1,0 +1,134 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Cases follow the pages' test plan (MLX pull request "[Metal] Add Flash Attention
+VJP for training", "Test Plan": vector path L = 1, 4, 7, 8; tiled L = 16 .. 256;
+head dims 32/64/128; GQA 4:1, 8:1, 16:1 and MHA; fp16/bf16/fp32; L = 1,
+non-power-of-two lengths, large batch, qL != kvL) at sizes the oracle finishes in
+seconds but that span several tiles and a ragged tail. Full-size workloads are in
+test_workloads_gpu.py.
+"""
+
+import numpy as np
+import pytest
+
+from parity_util import compare, reference, run_gpu
+from scaled_dot_product_online_amd import inputs as inp
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # fp32 operands (VALU path)
+    (1, 2, 2, 64, 64, 32, "f32", False),
+    (1, 4, 2, 100, 100, 64, "f32", True),
+    (2, 4, 1, 37, 150, 128, "f32", False),
+    (1, 2, 2, 1, 1, 64, "f32", True),
+]
+for _dt in ("f16", "bf16"):
+    for _d in (32, 64, 128):
+        CASES.append((1, 4, 2, 200, 200, _d, _dt, False))
+        CASES.append((1, 4, 2, 200, 200, _d, _dt, True))
+    CASES += [
+        (1, 2, 1, 70, 300, 64, _dt, False),     # Lq != Lkv, ragged on both axes
+        (2, 8, 1, 16, 16, 64, _dt, True),       # GQA 8:1, one partial tile
+        (1, 16, 1, 32, 32, 128, _dt, False),    # GQA 16:1
+        (1, 2, 2, 256, 256, 128, _dt, True),    # MHA, exact tiles
+        (1, 2, 2, 1, 1, 64, _dt, True),         # L = 1 causal (tiled path)
+        (1, 2, 2, 9, 9, 64, _dt, False),        # just above the vector cutoff
+        (32, 2, 1, 8, 8, 32, _dt, True),        # large batch, causal short rows
+        # vector path (Lq <= 8, not causal)
+        (2, 8, 2, 1, 1000, 64, _dt, False),
+        (2, 8, 2, 4, 1000, 64, _dt, False),
+        (2, 8, 2, 7, 333, 128, _dt, False),
+        (1, 8, 1, 4, 2085, 128, _dt, False),    # 32 packed rows, ragged keys
+        (3, 4, 4, 8, 1, 32, _dt, False),        # single key
+        (2, 16, 4, 8, 4099, 64, _dt, False),    # several splits
+    ]
+
+
+def _id(c):
+    B, Hq, Hkv, Lq, Lkv, D, dt, causal = c
+    return f"{dt}-B{B}-H{Hq}x{Hkv}-L{Lq}x{Lkv}-D{D}-{'causal' if causal else 'full'}"
+
+
+@pytest.mark.parametrize("case_def", CASES, ids=[_id(c) for c in CASES])
+def test_parity_native_out(case_def, device):
+    case = inp.make_case(*case_def, seed=0)
+    got = run_gpu(case, case.dtype, device)
+    compare(case, got, reference(case, case.dtype))
+
+
+@pytest.mark.parametrize("case_def", [c for c in CASES if c[6] != "f32"][::2],
+                         ids=[_id(c) for c in CASES if c[6] != "f32"][::2])
+def test_parity_fp32_out(case_def, device):
+    case = inp.make_case(*case_def, seed=1)
+    got = run_gpu(case, "f32", device)
+    compare(case, got, reference(case, "f32"))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_large_logits_and_rising_scores(dt, device):
+    """Scores ~N(0, 100), and keys whose norm grows along the sequence so the running max
+    moves in every tile; both stress the exp2-domain rescaling."""
+    case = inp.make_case(1, 4, 2, 300, 300, 64, dt, is_causal=True, seed=3)
+    case.q = inp.from_f32(inp.as_float64(case.q, dt).astype(np.float32) * 10.0, dt)
+    got = run_gpu(case, "f32", device)
+    compare(case, got, reference(case, "f32"))
+    case2 = inp.make_case(1, 2, 2, 64, 700, 64, dt, is_causal=False, seed=4)
+    k = inp.as_float64(case2.k, dt)
+    k *= np.linspace(0.2, 3.0, k.shape[2])[None, None, :, None]
+    case2.k = inp.from_f32(k.astype(np.float32), dt)
+    got2 = run_gpu(case2, "f32", device)
+    compare(case2, got2, reference(case2, "f32"))
+
+
+@pytest.mark.parametrize("case_def", [(2, 8, 2, 200, 200, 64, "bf16", True), (2, 8, 2, 4, 3000, 128, "f16", False),
+                                      (1, 4, 2, 100, 100, 64, "f32", True)])
+def test_forward_without_lse_matches(case_def, device):
+    import torch
+
+    import scaled_dot_product_online_amd as sd
+
+    case = inp.make_case(*case_def)
+    q, k, v = (inp.to_torch(getattr(case, n), case.dtype, device) for n in ("q", "k", "v"))
+    o1, lse = sd.sdpa_fwd(q, k, v, scale=case.scale, is_causal=case.is_causal)
+    o2, none = sd.sdpa_fwd(q, k, v, scale=case.scale, is_causal=case.is_causal, need_lse=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("case_def", [(1, 8, 2, 333, 333, 128, "bf16", True), (2, 8, 2, 8, 5000, 64, "f16", False),
+                                      (1, 2, 1, 70, 300, 32, "bf16", False)])
+def test_deterministic_and_canaries(case_def, device):
+    """Bitwise-identical repeats (no atomics anywhere) and no writes outside the outputs."""
+    import torch
+
+    import scaled_dot_product_online_amd as sd
+
+    case = inp.make_case(*case_def)
+    q, k, v, do = (inp.to_torch(getattr(case, n), case.dtype, device) for n in ("q", "k", "v", "do"))
+    tdt = q.dtype
+    pad = 4096
+    B, Hq, Lq, D = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+
+    def padded(shape, dtype):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * pad,), 7.0, dtype=dtype, device=device)
+        return buf, buf[pad:pad + n].view(shape)
+
+    runs = []
+    for _ in range(2):
+        ob, o = padded((B, Hq, Lq, D), tdt)
+        lb, lse = padded((B, Hq, Lq), torch.float32)
+        qb, dq = padded((B, Hq, Lq, D), tdt)
+        kb, dk = padded((B, Hkv, Lkv, D), tdt)
+        vb, dv = padded((B, Hkv, Lkv, D), tdt)
+        sd.sdpa_fwd(q, k, v, scale=case.scale, is_causal=case.is_causal, out=o, lse=lse)
+        sd.sdpa_bwd(q, k, v, o, lse, do, scale=case.scale, is_causal=case.is_causal, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        for buf in (ob, lb, qb, kb, vb):
+            assert torch.all(buf[:pad] == 7.0) and torch.all(buf[-pad:] == 7.0), "write outside an output"
+        runs.append([t.clone() for t in (o, lse, dq, dk, dv)])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b), "repeat differs"
