@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention hot path on one MI355X.
+
+A step is one pass of the whole path on one batch of synthetic input: the forward
+(O and the logsumexp) followed by the backward's two stages (dQ, then dK/dV), on
+the workload the headline metric is quoted on (bf16, GQA 8:1, causal, B=4,
+Hq=32, Hkv=4, L=4096, D=128; inputs i.i.d. N(0,1) from seed 0, resident in HBM
+before timing starts). FLOPs are counted as 4*B*Hq*Lq*Lkv*D for the forward and
+2.5x that for the backward, halved for causal masking.
+
+Prints ONE JSON line (rank 0, N=1). Besides the contract fields it carries:
+  roofline      the dominant kernel's algorithmic FLOPs per launch over its mean
+                launch time (HIP events on the launch stream) against dense MFMA peak
+  cpu_baseline  the fp64 oracle timed on this host on one GQA group of the workload
+  vector_path   the short-query path (Lq = 8, D = 128, Lkv = 8192) in HBM GB/s
+Options: --sweep prints one line per workload instead (no CPU baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from scaled_dot_product_online_amd import inputs as inp  # noqa: E402
+from scaled_dot_product_online_amd.workloads import BY_NAME, HEADLINE, WORKLOADS, flops  # noqa: E402
+
+METRIC = "SDPA TFLOP/s fwd & fwd+bwd (bf16/fp16, causal) and % of MFMA peak, 1 GPU"
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense, AMD's published MI355X figures
+PEAK_HBM_GBS = 8000.0
+VECTOR_WORKLOAD = "vec_bf16_lq8_d128"
+# GEMMs each kernel executes, in units of the forward's two (S and P.V):
+KERNEL_GEMMS = {"fwd": 2, "bwd_stage0": 3, "bwd_stage1": 4}  # dQ kernel: S, dP, dQ; dK/dV kernel: S, dP, dV, dK
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vector", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="one JSON line per workload")
+    return ap.parse_args()
+
+
+class Runner:
+    """Device buffers for one workload and a step() that runs fwd + bwd stage 0 + stage 1."""
+
+    def __init__(self, name, device):
+        import torch
+
+        import scaled_dot_product_online_amd as sd
+
+        self.sd, self.torch = sd, torch
+        self.name = name
+        _, B, Hq, Hkv, Lq, Lkv, D, dt, causal = BY_NAME[name]
+        self.case = inp.make_case(B, Hq, Hkv, Lq, Lkv, D, dt, is_causal=causal, seed=0)
+        c = self.case
+        self.q, self.k, self.v, self.do = (inp.to_torch(getattr(c, n), dt, device) for n in ("q", "k", "v", "do"))
+        tdt = self.q.dtype
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=device)
+        self.dq = torch.empty_like(self.q)
+        self.dk, self.dv = torch.empty_like(self.k), torch.empty_like(self.v)
+        code = {"f32": sd.F32, "f16": sd.F16, "bf16": sd.BF16}[dt]
+        self.path = sd.PATH_NAMES[sd.select_path(Hq, Hkv, Lq, Lkv, D, causal, code)]
+        wf = sd.workspace_bytes(0, B, Hq, Hkv, Lq, Lkv, D, causal, code)
+        wb = sd.workspace_bytes(1, B, Hq, Hkv, Lq, Lkv, D, causal, code)
+        self.ws_f = torch.empty(max(wf, 256), dtype=torch.uint8, device=device)
+        self.ws_b = torch.empty(max(wb, 256), dtype=torch.uint8, device=device)
+        self.stream = torch.cuda.current_stream(device)
+        self.tdt = tdt
+        self.fwd_flops = flops(B, Hq, Lq, Lkv, D, causal)
+        self.bwd_flops = flops(B, Hq, Lq, Lkv, D, causal, backward=True)
+        e = 2 if dt != "f32" else 4
+        qb, kb = B * Hq * Lq * D * e, B * Hkv * Lkv * D * e
+        lse_b = B * Hq * Lq * 4
+        # Algorithmic HBM bytes: each operand read once, each result written once.
+        self.fwd_bytes = qb + 2 * kb + qb + lse_b
+        self.bwd_bytes = (qb + 2 * kb + qb + qb + lse_b) + (qb + 2 * kb)
+
+    def fwd(self):
+        self.sd.sdpa_fwd(self.q, self.k, self.v, scale=self.case.scale, is_causal=self.case.is_causal, out=self.o,
+                         lse=self.lse, workspace=self.ws_f, stream=self.stream)
+
+    def bwd(self, stage):
+        self.sd.sdpa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, scale=self.case.scale,
+                         is_causal=self.case.is_causal, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_b,
+                         stream=self.stream, stage=stage)
+
+    def timed(self, steps, warmup):
+        """Wall time of `steps` steps (synchronised on both sides) and per-kernel event times."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.fwd()
+            self.bwd(0)
+            self.bwd(1)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(self.stream)
+            self.fwd()
+            ev[i][1].record(self.stream)
+            self.bwd(0)
+            ev[i][2].record(self.stream)
+            self.bwd(1)
+            ev[i][3].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = {"fwd": 0.0, "bwd_stage0": 0.0, "bwd_stage1": 0.0}
+        for e in ev:
+            ms["fwd"] += e[0].elapsed_time(e[1]) / steps
+            ms["bwd_stage0"] += e[1].elapsed_time(e[2]) / steps
+            ms["bwd_stage1"] += e[2].elapsed_time(e[3]) / steps
+        return wall, ms
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """fp64 oracle, fwd+bwd, on whole GQA groups of the same inputs, timed on host cores.
+
+    Groups (b, hk) are taken in order until ~budget_s seconds of CPU work or all are done."""
+    from oracle import sdpa_reference as ref
+
+    try:
+        import threadpoolctl
+
+        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    G = case.Hq // case.Hkv
+    groups = [(b, hk) for b in range(case.B) for hk in range(case.Hkv)]
+    done, elapsed = 0, 0.0
+    for b, hk in groups:
+        q = case.f64("q")[b:b + 1, hk * G:(hk + 1) * G]
+        k = case.f64("k")[b:b + 1, hk:hk + 1]
+        v = case.f64("v")[b:b + 1, hk:hk + 1]
+        do = case.f64("do")[b:b + 1, hk * G:(hk + 1) * G]
+        t0 = time.perf_counter()
+        ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    f = done * (flops(1, G, case.Lq, case.Lkv, case.D, case.is_causal)
+                + flops(1, G, case.Lq, case.Lkv, case.D, case.is_causal, backward=True))
+    return {"value": f / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy oracle fwd+bwd of {done} of {len(groups)} GQA groups ({G} query heads each, "
+                      f"L={case.Lq}, D={case.D}, causal={case.is_causal}) of the same workload; {elapsed:.1f} s of "
+                      f"CPU work; FLOPs counted as for the GPU"}
+
+
+def measure(runner, steps, warmup):
+    wall, ms = runner.timed(steps, warmup)
+    total = runner.fwd_flops + runner.bwd_flops
+    value = total * steps / wall / 1e12
+    dt = runner.case.dtype
+    out = {"value": value, "ms_per_step": wall / steps * 1e3, "kernel_ms": ms,
+           "fwd_tflops": runner.fwd_flops / (ms["fwd"] * 1e-3) / 1e12,
+           "bwd_tflops": runner.bwd_flops / ((ms["bwd_stage0"] + ms["bwd_stage1"]) * 1e-3) / 1e12}
+    out["fwd_frac_of_peak"] = out["fwd_tflops"] / PEAK_MFMA_TFLOPS[dt]
+    out["fwdbwd_frac_of_peak"] = value / PEAK_MFMA_TFLOPS[dt]
+    dom = max(ms, key=ms.get)
+    if runner.path == "vector":
+        algo = {"fwd": runner.fwd_bytes, "bwd_stage0": runner.bwd_bytes, "bwd_stage1": 0}[dom]
+        ach = algo / (ms[dom] * 1e-3) / 1e9
+        out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": ach / PEAK_HBM_GBS, "traffic": None}
+    else:
+        algo = runner.fwd_flops * KERNEL_GEMMS[dom] / 2
+        ach = algo / (ms[dom] * 1e-3) / 1e12
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS[dt],
+                           "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_TFLOPS[dt], "traffic": None}
+    return out
+
+
+def vector_line(device, steps, warmup):
+    r = Runner(VECTOR_WORKLOAD, device)
+    _, ms = r.timed(steps, warmup)
+    fwd_gbs = r.fwd_bytes / (ms["fwd"] * 1e-3) / 1e9
+    bwd_gbs = r.bwd_bytes / ((ms["bwd_stage0"] + ms["bwd_stage1"]) * 1e-3) / 1e9
+    return {"workload": VECTOR_WORKLOAD, "kernel_ms": ms, "fwd_GBps": fwd_gbs, "bwd_GBps": bwd_gbs,
+            "fwd_frac_of_hbm_peak": fwd_gbs / PEAK_HBM_GBS, "bwd_frac_of_hbm_peak": bwd_gbs / PEAK_HBM_GBS}
+
+
+def config_of(name):
+    _, B, Hq, Hkv, Lq, Lkv, D, dt, causal = BY_NAME[name]
+    return {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": causal,
+            "scale": "1/sqrt(D)", "inputs": "iid N(0,1), numpy default_rng(0)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the (b, kv-head) groups are "
+              "independent; see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    device = "cuda:0"
+    names = [w[0] for w in WORKLOADS] if args.sweep else [args.workload]
+    for name in names:
+        r = Runner(name, device)
+        m = measure(r, args.steps, args.warmup)
+        line = {"metric": METRIC, "value": m["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": r.case.dtype, "data": "synthetic",
+                "config": config_of(name), "path": r.path, "fwd_tflops": m["fwd_tflops"],
+                "bwd_tflops": m["bwd_tflops"], "fwd_frac_of_peak": m["fwd_frac_of_peak"],
+                "fwdbwd_frac_of_peak": m["fwdbwd_frac_of_peak"], "kernel_ms": m["kernel_ms"],
+                "roofline": m["roofline"]}
+        if not args.sweep:
+            if not args.no_vector:
+                line["vector_path"] = vector_line(device, args.steps, args.warmup)
+            line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(r.case)
+        print(json.dumps(line), flush=True)
+        del r
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

@@ -65,7 +65,7 @@ typedef enum {
   SDPA_ERR_WORKSPACE = 4,   /* workspace smaller than sdpa_workspace_bytes()            */
   SDPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte (workspace: 256) aligned   */
   SDPA_ERR_DEVICE = 6,      /* the HIP runtime rejected a launch                        */
-  SDPA_ERR_VALUE = 7        /* scale is not finite                                      */
+  SDPA_ERR_VALUE = 7        /* scale is not finite, or an invalid stage number          */
 } sdpa_status_t;
 
 /* Kernel families, as returned by sdpa_select_path(). */
@@ -123,6 +123,22 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
                        void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
                        int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward as two stream-ordered stages; sdpa_bwd(...) is stage 0 followed
+ * by stage 1 with the same arguments. Stage 1 must be enqueued after stage 0 on
+ * the same stream with the same workspace, which carries state between them.
+ *   tiled and fp32 paths: stage 0 writes dq (and Delta_i = sum_d dO_id O_id
+ *                         into the workspace); stage 1 writes dk and dv.
+ *   vector path:          stage 0 writes dk, dv and per-split dq partials (in
+ *                         the workspace); stage 1 reduces them into dq.
+ * Arguments, validation and errors are those of sdpa_bwd; `stage` must be 0 or 1
+ * (else SDPA_ERR_VALUE). Useful to time or schedule the two halves separately.
+ */
+sdpa_status_t sdpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                             int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype,
+                             sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static string naming a status code. Never NULL. */
 const char* sdpa_status_str(sdpa_status_t status);

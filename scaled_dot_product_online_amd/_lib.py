@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libsdpa_mi355x.so")
 F32, F16, BF16 = 0, 1, 2
 PATH_TILED, PATH_VECTOR, PATH_FP32 = 0, 1, 2
 PATH_NAMES = {PATH_TILED: "tiled", PATH_VECTOR: "vector", PATH_FP32: "fp32"}
-SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_status_str")
+SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_stage", "sdpa_status_str")
 
 _lib = None
 
@@ -48,6 +48,8 @@ def library():
     lib.sdpa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, c_int, c_int,
                              c_int, vp, ctypes.c_size_t, vp]
     lib.sdpa_bwd.restype = c_int
+    lib.sdpa_bwd_stage.argtypes = [c_int] + lib.sdpa_bwd.argtypes
+    lib.sdpa_bwd_stage.restype = c_int
     lib.sdpa_status_str.argtypes = [c_int]
     lib.sdpa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -138,8 +140,11 @@ def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True
 
 
 def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
-    """dQ, dK, dV of sum(O * dO); ``o`` and ``lse`` are what sdpa_fwd returned."""
+             workspace=None, stream=None, stage=None):
+    """dQ, dK, dV of sum(O * dO); ``o`` and ``lse`` are what sdpa_fwd returned.
+
+    ``stage`` None runs the whole backward; 0 or 1 runs one stage (sdpa_bwd_stage),
+    in which case the same ``workspace`` must be passed to both stages."""
     import torch
 
     _contig(q, k, v, o, lse, dO)
@@ -156,8 +161,9 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
     nws = workspace_bytes(1, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
     if workspace is None:
         workspace = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
-    st = library().sdpa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
-                            B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)), dt, odt, _ptr(workspace),
-                            workspace.numel(), _stream(q.device, stream))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)), dt, odt, _ptr(workspace), workspace.numel(),
+            _stream(q.device, stream))
+    st = library().sdpa_bwd(*args) if stage is None else library().sdpa_bwd_stage(int(stage), *args)
     _check(st)
     return dq, dk, dv

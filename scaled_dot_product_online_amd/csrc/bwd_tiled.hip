@@ -398,16 +398,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const uint16_t* __rest
 
 template <typename T, int D, bool C, typename OutT>
 hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                        const void* dO, void* dq, void* dk, void* dv, float* delta, float scale, hipStream_t st) {
+                        const void* dO, void* dq, void* dk, void* dv, float* delta, float scale, int stages,
+                        hipStream_t st) {
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int G = (int)(s.Hq / s.Hkv);
-  const int n_qblk = (int)((s.Lq + kDqBM - 1) / kDqBM);
-  const int n_bh = (int)(s.B * s.Hq);
-  hipLaunchKernelGGL((dq_kernel<T, D, C, OutT>), dim3(n_qblk * n_bh), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse, (const uint16_t*)dO, (OutT*)dq,
-                     delta, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (stages & kStage0) {
+    const int n_qblk = (int)((s.Lq + kDqBM - 1) / kDqBM);
+    const int n_bh = (int)(s.B * s.Hq);
+    hipLaunchKernelGGL((dq_kernel<T, D, C, OutT>), dim3(n_qblk * n_bh), dim3(kThreads), 0, st, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse, (const uint16_t*)dO, (OutT*)dq,
+                       delta, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(stages & kStage1)) return hipSuccess;
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
   hipLaunchKernelGGL((dkv_kernel<T, D, C, OutT>), dim3(n_kblk * n_bhk), dim3(kThreads), 0, st, (const uint16_t*)q,
@@ -419,11 +423,11 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
 template <typename T, typename OutT>
 hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dO, void* dq, void* dk, void* dv, float* delta, float scale,
-                    hipStream_t st) {
-#define SDPA_BWD_CASE(DV)                                                                                        \
-  case DV:                                                                                                       \
-    return causal ? launch_typed<T, DV, true, OutT>(s, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, st)       \
-                  : launch_typed<T, DV, false, OutT>(s, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, st);
+                    int stages, hipStream_t st) {
+#define SDPA_BWD_CASE(DV)                                                                                          \
+  case DV:                                                                                                         \
+    return causal ? launch_typed<T, DV, true, OutT>(s, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st) \
+                  : launch_typed<T, DV, false, OutT>(s, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
   switch (s.D) {
     SDPA_BWD_CASE(32)
     SDPA_BWD_CASE(64)
@@ -438,13 +442,13 @@ hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, c
 
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                            float* delta, float scale, hipStream_t st) {
+                            float* delta, float scale, int stages, hipStream_t st) {
   if (dt == kBF16)
-    return out == kF32 ? launch_d<bf16_t, float>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, st)
-                       : launch_d<bf16_t, bf16_t>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, st);
+    return out == kF32 ? launch_d<bf16_t, float>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
+                       : launch_d<bf16_t, bf16_t>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
   if (dt == kF16)
-    return out == kF32 ? launch_d<f16_t, float>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, st)
-                       : launch_d<f16_t, f16_t>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, st);
+    return out == kF32 ? launch_d<f16_t, float>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
+                       : launch_d<f16_t, f16_t>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
   return hipErrorInvalidValue;
 }
 

@@ -245,15 +245,18 @@ hipError_t fwd_typed(const Shape& s, const float* q, const float* k, const float
 
 template <int D, bool C>
 hipError_t bwd_typed(const Shape& s, const float* q, const float* k, const float* v, const float* lse,
-                     const float* dO, const float* delta, float* dq, float* dk, float* dv, float scale,
+                     const float* dO, const float* delta, float* dq, float* dk, float* dv, float scale, int stages,
                      hipStream_t st) {
   constexpr int ROWS = kF32Threads / (D / 32);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((dq_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
-                     delta, dq, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, scale_log2, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (stages & kStage0) {
+    const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((dq_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
+                       delta, dq, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, scale_log2, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(stages & kStage1)) return hipSuccess;
   const int n_kblk = (int)((s.Lkv + ROWS - 1) / ROWS);
   hipLaunchKernelGGL((dkv_f32_kernel<D, C>), dim3(n_kblk * s.B * s.Hkv), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
                      delta, dk, dv, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_kblk, scale_log2, scale);
@@ -274,13 +277,15 @@ hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const flo
 
 hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* dO, float* dq, float* dk, float* dv,
-                          float* delta, float scale, hipStream_t st) {
-  hipError_t e = launch_delta(s, kF32, kF32, o, dO, delta, st);
-  if (e != hipSuccess) return e;
+                          float* delta, float scale, int stages, hipStream_t st) {
+  if (stages & kStage0) {
+    hipError_t e = launch_delta(s, kF32, kF32, o, dO, delta, st);
+    if (e != hipSuccess) return e;
+  }
   switch (s.D) {
-    case 32: return causal ? bwd_typed<32, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st) : bwd_typed<32, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st);
-    case 64: return causal ? bwd_typed<64, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st) : bwd_typed<64, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st);
-    case 128: return causal ? bwd_typed<128, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st) : bwd_typed<128, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, st);
+    case 32: return causal ? bwd_typed<32, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<32, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 64: return causal ? bwd_typed<64, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<64, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 128: return causal ? bwd_typed<128, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<128, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -14,6 +14,9 @@ struct Shape {
   int64_t B, Hq, Hkv, Lq, Lkv, D;
 };
 
+// Backward stages (bit mask): stage 0 and stage 1 as documented for sdpa_bwd_stage.
+enum { kStage0 = 1, kStage1 = 2, kStagesAll = 3 };
+
 // Delta_i = sum_d dO[i,d] * O[i,d] over all B*Hq*Lq rows (delta.hip).
 hipError_t launch_delta(const Shape& s, Dt o_dt, Dt do_dt, const void* o, const void* dO, float* delta,
                         hipStream_t st);
@@ -25,14 +28,14 @@ hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const vo
 // Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is [B*Hq*Lq] fp32 scratch.
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                            float* delta, float scale, hipStream_t st);
+                            float* delta, float scale, int stages, hipStream_t st);
 
 // float32 path (fp32_path.hip).
 hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v, float* o,
                           float* lse, float scale, hipStream_t st);
 hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* dO, float* dq, float* dk, float* dv,
-                          float* delta, float scale, hipStream_t st);
+                          float* delta, float scale, int stages, hipStream_t st);
 
 // Short-query path (vector_path.hip).
 int vector_num_splits(const Shape& s);
@@ -42,6 +45,6 @@ hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const
                              float* lse, float scale, void* ws, hipStream_t st);
 hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
-                             float scale, hipStream_t st);
+                             float scale, int stages, hipStream_t st);
 
 }  // namespace sdpa

@@ -107,10 +107,14 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
   }
 }
 
-sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
-                       void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
-                       int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
+                      int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   sdpa_status_t st = check_shape(B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype, out_dtype);
   if (st != SDPA_OK) return st;
   if (!isfinite(scale)) return SDPA_ERR_VALUE;
@@ -130,14 +134,35 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
     case SDPA_PATH_FP32:
       return device_status(sdpa::launch_bwd_f32(s, causal, (const float*)q, (const float*)k, (const float*)v,
                                                 (const float*)o, lse, (const float*)dO, (float*)dq, (float*)dk,
-                                                (float*)dv, delta, scale, hs));
+                                                (float*)dv, delta, scale, stages, hs));
     case SDPA_PATH_VECTOR:
       return device_status(sdpa::launch_bwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, q, k, v, o, lse, dO, dq,
-                                                   dk, dv, workspace, scale, hs));
+                                                   dk, dv, workspace, scale, stages, hs));
     default:
       return device_status(sdpa::launch_bwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse,
-                                                  dO, dq, dk, dv, delta, scale, hs));
+                                                  dO, dq, dk, dv, delta, scale, stages, hs));
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                       void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
+                       int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(sdpa::kStagesAll, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal, dtype,
+                 out_dtype, workspace, workspace_bytes, stream);
+}
+
+sdpa_status_t sdpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                             int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype,
+                             sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage != 0 && stage != 1) return SDPA_ERR_VALUE;
+  return run_bwd(stage == 0 ? sdpa::kStage0 : sdpa::kStage1, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
+                 scale, is_causal, dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 const char* sdpa_status_str(sdpa_status_t status) {

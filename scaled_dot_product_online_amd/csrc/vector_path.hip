@@ -527,18 +527,21 @@ hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v
 
 template <typename T, int D, typename OutT>
 hipError_t bwd_typed(const Shape& s, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                     const void* dO, void* dq, void* dk, void* dv, void* ws, float scale, hipStream_t st) {
+                     const void* dO, void* dq, void* dk, void* dv, void* ws, float scale, int stages, hipStream_t st) {
   const SplitPlan pl = plan(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int64_t tr = rows_total(s);
   float* dq_part = (float*)ws;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL((vec_bwd_kernel<T, D, OutT>), dim3(pl.nsplit * s.B * s.Hkv), dim3(kThreads), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
-                     (const uint16_t*)dO, (OutT*)dk, (OutT*)dv, dq_part, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv,
-                     pl.nsplit, (int)pl.split_len, tr, scale_log2, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (stages & kStage0) {
+    hipLaunchKernelGGL((vec_bwd_kernel<T, D, OutT>), dim3(pl.nsplit * s.B * s.Hkv), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
+                       (const uint16_t*)dO, (OutT*)dk, (OutT*)dv, dq_part, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv,
+                       pl.nsplit, (int)pl.split_len, tr, scale_log2, scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(stages & kStage1)) return hipSuccess;
   const int64_t n4 = tr * (D / 4);
   hipLaunchKernelGGL((vec_dq_reduce_kernel<D, OutT>), dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, st, (const float*)dq_part, (OutT*)dq, tr, pl.nsplit, scale);
@@ -578,9 +581,9 @@ hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const
 
 hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
-                             float scale, hipStream_t st) {
+                             float scale, int stages, hipStream_t st) {
   if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
-  SDPA_VEC_DISPATCH(bwd_typed, s, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, st)
+  SDPA_VEC_DISPATCH(bwd_typed, s, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
 }
 
 }  // namespace sdpa
