@@ -11,7 +11,7 @@ before timing starts). FLOPs are counted as 4*B*Hq*Lq*Lkv*D for the forward and
 Prints ONE JSON line (rank 0, N=1). Besides the contract fields it carries:
   roofline      the dominant kernel's algorithmic FLOPs per launch over its mean
                 launch time (HIP events on the launch stream) against dense MFMA peak
-  cpu_baseline  the fp64 oracle timed on this host on one GQA group of the workload
+  cpu_baseline  the fp64 oracle timed on this host on whole GQA groups of the workload
   vector_path   the short-query path (Lq = 8, D = 128, Lkv = 8192) in HBM GB/s
 Options: --sweep prints one line per workload instead (no CPU baseline).
 """
@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vector", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run 3 plain device copies of MIB MiB (reference for HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -173,13 +175,45 @@ def measure(runner, steps, warmup):
         algo = {"fwd": runner.fwd_bytes, "bwd_stage0": runner.bwd_bytes, "bwd_stage1": 0}[dom]
         ach = algo / (ms[dom] * 1e-3) / 1e9
         out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": ach / PEAK_HBM_GBS, "traffic": None}
+                           "frac": ach / PEAK_HBM_GBS, "traffic": measured_traffic(runner, dom)}
     else:
         algo = runner.fwd_flops * KERNEL_GEMMS[dom] / 2
         ach = algo / (ms[dom] * 1e-3) / 1e12
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS[dt],
-                           "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_TFLOPS[dt], "traffic": None}
+                           "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_TFLOPS[dt],
+                           "traffic": measured_traffic(runner, dom)}
     return out
+
+
+def kernel_symbol(runner, label):
+    """Short kernel name (as rocprofv3 summaries print it) behind a bench label."""
+    c = runner.case
+    t = {"bf16": "bf16_t", "f16": "f16_t", "f32": "float"}[c.dtype]
+    causal = "true" if c.is_causal else "false"
+    if runner.path == "tiled":
+        base = {"fwd": "fwd_tiled_kernel", "bwd_stage0": "dq_kernel", "bwd_stage1": "dkv_kernel"}[label]
+        return f"{base}<{t}, {c.D}, {causal}, {t}>"
+    if runner.path == "vector":
+        base = {"fwd": "vec_fwd_kernel", "bwd_stage0": "vec_bwd_kernel", "bwd_stage1": "vec_dq_reduce_kernel"}[label]
+        return f"{base}<{t}, {c.D}, {t}>"
+    return None
+
+
+def measured_traffic(runner, label):
+    """HBM bytes per launch from committed counter summaries, if taken on the current kernel sources."""
+    import glob
+
+    from scaled_dot_product_online_amd.rocprof_summary import sources_sha256
+
+    sym = kernel_symbol(runner, label)
+    sha = sources_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.json"))):
+        with open(path) as f:
+            t = json.load(f)
+        if t.get("source_sha256") == sha and sym in t.get("kernels", {}):
+            k = t["kernels"][sym]
+            return k["read_bytes"] + k["write_bytes"]
+    return None
 
 
 def vector_line(device, steps, warmup):
@@ -209,6 +243,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     device = "cuda:0"
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     names = [w[0] for w in WORKLOADS] if args.sweep else [args.workload]
     for name in names:
         r = Runner(name, device)
