@@ -60,7 +60,8 @@ typedef enum { SDPA_F32 = 0, SDPA_F16 = 1, SDPA_BF16 = 2 } sdpa_dtype_t;
 typedef enum {
   SDPA_OK = 0,
   SDPA_ERR_NULL = 1,        /* a required pointer is NULL                              */
-  SDPA_ERR_SHAPE = 2,       /* a size < 1, Hq % Hkv != 0, or element counts overflow    */
+  SDPA_ERR_SHAPE = 2,       /* a size < 1, Hq % Hkv != 0, counts overflow, or one head's
+                               (L + 256) * D elements exceed 2 GiB                     */
   SDPA_ERR_UNSUPPORTED = 3, /* D not in {32, 64, 128}, causal with Lq != Lkv, bad dtype */
   SDPA_ERR_WORKSPACE = 4,   /* workspace smaller than sdpa_workspace_bytes()            */
   SDPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte (workspace: 256) aligned   */

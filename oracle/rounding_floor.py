@@ -16,11 +16,12 @@ What is modelled (the kernel's rounding points, nothing else)
 -------------------------------------------------------------
 Forward, with the scores kept exact:
 * the probabilities that enter the P.V product are rounded to the operand dtype
-  *relative to the running maximum in force when their key block was processed*
+  *relative to the reference maximum in force when their key block was processed*
   (online softmax; MLX pull request "[Metal] Add Flash Attention VJP for
   training", section "Implementation Notes", log2-domain exponentials). The
-  running maximum restarts at every ``kv_segment`` keys and advances every
-  ``kv_block`` keys; the unrounded exponentials form the denominator;
+  reference restarts at every ``kv_segment`` keys and may move every ``kv_block``
+  keys, when the block's maximum exceeds it by more than ``slack``; the
+  unrounded exponentials form the denominator;
 * the output is rounded to the output dtype.
 Backward:
 * Delta_i uses the *stored* (rounded) forward output, as the kernel does;
@@ -60,8 +61,12 @@ def round_to(x, dtype):
     raise ValueError(f"unknown dtype {dtype!r}; expected one of {_DTYPES}")
 
 
-def _running_max(s, kv_block, kv_segment):
-    """Per score element, the running row maximum in force when its key block is processed."""
+def _running_max(s, kv_block, kv_segment, slack=0.0):
+    """Per score element, the row's reference maximum in force when its key block is processed.
+
+    The reference starts at -inf at every segment start and is replaced by a block's
+    maximum when that maximum exceeds it by more than ``slack`` (natural-log units);
+    with slack 0 this is the ordinary running maximum."""
     n, L = s.shape
     nblk = -(-L // kv_block)
     pad = np.full((n, nblk * kv_block), -np.inf)
@@ -72,11 +77,15 @@ def _running_max(s, kv_block, kv_segment):
         raise ValueError("kv_segment must be a multiple of kv_block")
     run = np.empty_like(bmax)
     for s0 in range(0, nblk, seg_blocks):
-        run[:, s0:s0 + seg_blocks] = np.maximum.accumulate(bmax[:, s0:s0 + seg_blocks], axis=1)
+        m = np.full(n, -np.inf)
+        for j in range(s0, min(s0 + seg_blocks, nblk)):
+            m = np.where(bmax[:, j] > m + slack, bmax[:, j], m)
+            run[:, j] = m
     return np.repeat(run, kv_block, axis=1)[:, :L]
 
 
-def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None, rows=None):
+def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None, rows=None,
+                         slack=0.0):
     """Modelled kernel output O (already rounded to ``out_dtype``) for one head."""
     qh, kh, vh = (np.asarray(a, dtype=np.float64) for a in (qh, kh, vh))
     if rows is None:
@@ -86,7 +95,7 @@ def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_b
     if is_causal:
         s = np.where(np.arange(kh.shape[0])[None, :] <= rows[:, None], s, -np.inf)
     m_final = s.max(axis=1, keepdims=True)
-    m_run = _running_max(s, kv_block, kv_segment)
+    m_run = _running_max(s, kv_block, kv_segment, slack)
     with np.errstate(invalid="ignore"):
         p_tilde = np.where(np.isfinite(s), np.exp(s - m_run), 0.0)
         w = np.where(np.isfinite(m_run), np.exp(m_run - m_final), 0.0)
@@ -95,7 +104,7 @@ def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_b
     return round_to((r @ vh) / denom, out_dtype)
 
 
-def emulate_forward(q, k, v, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None):
+def emulate_forward(q, k, v, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None, slack=0.0):
     """Modelled kernel output O [B,Hq,Lq,D], rounded to ``out_dtype``."""
     B, Hq = q.shape[:2]
     G = Hq // k.shape[1]
@@ -103,7 +112,7 @@ def emulate_forward(q, k, v, scale, is_causal, op_dtype, out_dtype, kv_block, kv
     for b in range(B):
         for h in range(Hq):
             o[b, h] = emulate_forward_head(q[b, h], k[b, h // G], v[b, h // G], scale, is_causal,
-                                           op_dtype, out_dtype, kv_block, kv_segment)
+                                           op_dtype, out_dtype, kv_block, kv_segment, slack=slack)
     return o
 
 

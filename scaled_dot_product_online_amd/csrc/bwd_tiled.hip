@@ -11,16 +11,18 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
 //
 // Kernel 1 (dq_kernel): one workgroup = 4 waves x 32 query rows of one (b, hq).
-//   It first forms Delta for its rows from O and dO and stores it for kernel 2,
-//   then streams K/V tiles of 64 keys through LDS. Like the forward it works on
+//   It first forms Delta for its rows from O and dO and stores {LSE*log2e, Delta}
+//   per query in the workspace for kernel 2, then streams K/V tiles of 64 keys
+//   through double-buffered, swizzled LDS filled by direct buffer-to-LDS loads. Like the forward it works on
 //   transposed scores (S^T = K Q^T, dP^T = V dO^T) so that each lane owns one
 //   query row; dQ^T += K^T dS^T reads K^T with the LDS transpose read.
-// Kernel 2 (dkv_kernel): one workgroup = 4 waves x 32 key rows of one (b, hk);
+// Kernel 2 (dkv_kernel): one workgroup = 8 waves x 16 key rows of one (b, hk);
 //   the waves keep K and V of their rows in registers and accumulate dK and dV
 //   while streaming Q/dO tiles of 64 queries of every query head of the group.
-//   Scores are computed as S = Q K^T (lane owns one key column), which puts P
-//   and dS directly in the B-operand layout of dV^T += dO^T P and
-//   dK^T += Q^T dS; dO^T and Q^T are read with the LDS transpose read.
+//   Scores are computed as S = Q K^T on 16x16x32 tiles (lane owns one key
+//   column), which puts P and dS directly in the B-operand layout of
+//   dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are read with the LDS
+//   transpose read.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,100 +31,89 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <typename OutT>
+__device__ __forceinline__ void load_out8(rsrc_t r, uint32_t elem, float* x);
+template <>
+__device__ __forceinline__ void load_out8<float>(rsrc_t r, uint32_t elem, float* x) {
+  const u32x4_t a = buf_load16(r, elem * 4), b = buf_load16(r, elem * 4 + 16);
+  for (int i = 0; i < 4; ++i) {
+    x[i] = __uint_as_float(a[i]);
+    x[4 + i] = __uint_as_float(b[i]);
+  }
+}
+template <typename T16>
+__device__ __forceinline__ void load_out8_16(rsrc_t r, uint32_t elem, float* x) {
+  const u32x4_t w = buf_load16(r, elem * 2);
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = lo_f32<T16>(w[i]);
+    x[2 * i + 1] = hi_f32<T16>(w[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void load_out8<bf16_t>(rsrc_t r, uint32_t elem, float* x) {
+  load_out8_16<bf16_t>(r, elem, x);
+}
+template <>
+__device__ __forceinline__ void load_out8<f16_t>(rsrc_t r, uint32_t elem, float* x) {
+  load_out8_16<f16_t>(r, elem, x);
+}
+
 // ---------------------------------------------------------------------------------
-// dQ (+ Delta)
+// Stage 0: dQ, plus the per-query {LSE*log2e, Delta} pairs for stage 1
 // ---------------------------------------------------------------------------------
 constexpr int kDqBM = 128;  // query rows per workgroup
 constexpr int kDqBN = 64;   // keys per tile
 
-template <int D>
-struct DqTile {
-  static constexpr int KP = D + 8;  // 16-byte skew
-  static constexpr int VP = D + 8;
-  static constexpr int CPR = D / 8;
-  static constexpr int RPP = kThreads / CPR;
-  static constexpr int PASSES = kDqBN / RPP;
-};
-
-template <typename OutT>
-__device__ __forceinline__ void load_out8(const OutT* p, float* x);
-template <>
-__device__ __forceinline__ void load_out8<float>(const float* p, float* x) {
-  const f32x4_t a = *(const f32x4_t*)p, b = *(const f32x4_t*)(p + 4);
-  for (int i = 0; i < 4; ++i) {
-    x[i] = a[i];
-    x[4 + i] = b[i];
-  }
-}
-template <>
-__device__ __forceinline__ void load_out8<bf16_t>(const bf16_t* p, float* x) {
-  const u32x4_t w = gload16B(p);
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = lo_f32<bf16_t>(w[i]);
-    x[2 * i + 1] = hi_f32<bf16_t>(w[i]);
-  }
-}
-template <>
-__device__ __forceinline__ void load_out8<f16_t>(const f16_t* p, float* x) {
-  const u32x4_t w = gload16B(p);
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = lo_f32<f16_t>(w[i]);
-    x[2 * i + 1] = hi_f32<f16_t>(w[i]);
-  }
-}
-
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kThreads, 1) void dq_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, const OutT* __restrict__ o,
                                                          const float* __restrict__ lse,
                                                          const uint16_t* __restrict__ dO, OutT* __restrict__ dq,
-                                                         float* __restrict__ delta, int Hq, int G, int Lq, int Lkv,
-                                                         int n_qblk, int n_bh, float scale_log2, float scale) {
-  using TL = DqTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kDqBN * TL::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kDqBN * TL::VP];
+                                                         f32x2_t* __restrict__ rowstat, int Hq, int G, int Lq,
+                                                         int Lkv, int n_qblk, int n_bh, int lq_pad,
+                                                         float scale_log2, float scale) {
+  using TL = SwzTile<D>;
+  constexpr int TILE = kDqBN * TL::RB;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];  // [buffer][K, V]
 
-  int qblk = blockIdx.x / n_bh;
-  const int bh = blockIdx.x - qblk * n_bh;
+  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh, G);
+  int qblk = wid / n_bh;
+  const int bh = wid - qblk * n_bh;
   if (CAUSAL) qblk = n_qblk - 1 - qblk;
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hk = hq / G, Hkv = Hq / G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
   const int q0 = qblk * kDqBM + wave * 32;
   const int qrow = q0 + n;
-  const bool row_ok = qrow < Lq;
-  const int64_t row_off = ((int64_t)bh * Lq + (row_ok ? qrow : 0)) * D;
 
   const int64_t kvoff = (int64_t)(b * Hkv + hk) * Lkv * D;
-  const uint16_t* kh = k + kvoff;
-  const uint16_t* vh = v + kvoff;
+  const int64_t qoff = (int64_t)bh * Lq * D;
+  const rsrc_t rq = make_rsrc(q + qoff, (uint32_t)Lq * D * 2);
+  const rsrc_t rdo = make_rsrc(dO + qoff, (uint32_t)Lq * D * 2);
+  const rsrc_t ro = make_rsrc(o + qoff, (uint32_t)Lq * D * (uint32_t)sizeof(OutT));
 
-  // Q^T and dO^T B operands; Delta from the stored O (this lane's half of the row).
+  // Q^T and dO^T B operands; Delta from the stored O over this lane's half of the row.
   u32x4_t qop[D / 16], doop[D / 16];
   float dpart = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const int d0 = 16 * c + 8 * g;
-    if (row_ok) {
-      qop[c] = gload16B(q + row_off + d0);
-      doop[c] = gload16B(dO + row_off + d0);
-      float ov[8];
-      load_out8<OutT>(o + row_off + d0, ov);
+    const uint32_t e = (uint32_t)(qrow * D + 16 * c + 8 * g);
+    qop[c] = buf_load16(rq, e * 2);
+    doop[c] = buf_load16(rdo, e * 2);
+    float ov[8];
+    load_out8<OutT>(ro, e, ov);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dpart = fmaf(lo_f32<T>(doop[c][w]), ov[2 * w], dpart);
-        dpart = fmaf(hi_f32<T>(doop[c][w]), ov[2 * w + 1], dpart);
-      }
-    } else {
-      qop[c] = (u32x4_t){0u, 0u, 0u, 0u};
-      doop[c] = (u32x4_t){0u, 0u, 0u, 0u};
+    for (int w = 0; w < 4; ++w) {
+      dpart = fmaf(lo_f32<T>(doop[c][w]), ov[2 * w], dpart);
+      dpart = fmaf(hi_f32<T>(doop[c][w]), ov[2 * w + 1], dpart);
     }
   }
   const float dlt = half_swap_sum(dpart);
+  const bool row_ok = qrow < Lq;
   const float lse2 = row_ok ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
-  if (row_ok && g == 0) delta[(int64_t)bh * Lq + qrow] = dlt;
+  if (row_ok && g == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, dlt};
 
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -132,52 +123,49 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const uint16_t* __restr
 
   const int kv_end = CAUSAL ? min(Lkv, qblk * kDqBM + kDqBM) : Lkv;
   const int ntiles = (kv_end + kDqBN - 1) / kDqBN;
-  const int ld_row = tid / TL::CPR, ld_col = (tid % TL::CPR) * 8;
-  u32x4_t kbuf[TL::PASSES], vbuf[TL::PASSES];
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int p = 0; p < TL::PASSES; ++p) {
-      const int r = t * kDqBN + p * TL::RPP + ld_row;
-      if (r < Lkv) {
-        kbuf[p] = gload16B(kh + (int64_t)r * D + ld_col);
-        vbuf[p] = gload16B(vh + (int64_t)r * D + ld_col);
-      } else {
-        kbuf[p] = (u32x4_t){0u, 0u, 0u, 0u};
-        vbuf[p] = (u32x4_t){0u, 0u, 0u, 0u};
-      }
-    }
-  };
+  const int key_lim = CAUSAL ? min(Lkv, qrow + 1) : Lkv;
   const int G16 = lane >> 4, L16 = lane & 15;
-  fetch(0);
+  const int fk = TL::f(n);
+  const int trow = 4 * g + (L16 >> 2);
+  const int ft = TL::f(trow), ft8 = TL::f(trow + 8);  // swizzle of the two rows each transposed read pair uses
+  const int tx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
+
+  const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
+  const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
+  TL::template dma_fill<kDqBN>(rk, lds, 0, wave, 4, lane);
+  TL::template dma_fill<kDqBN>(rv, lds + TILE, 0, wave, 4, lane);
   for (int t = 0; t < ntiles; ++t) {
+    wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int p = 0; p < TL::PASSES; ++p) {
-      const int r = p * TL::RPP + ld_row;
-      lds_write16B(k_lds + r * TL::KP + ld_col, kbuf[p]);
-      lds_write16B(v_lds + r * TL::VP + ld_col, vbuf[p]);
+    if (t + 1 < ntiles) {
+      uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
+      TL::template dma_fill<kDqBN>(rk, nb, (t + 1) * kDqBN, wave, 4, lane);
+      TL::template dma_fill<kDqBN>(rv, nb + TILE, (t + 1) * kDqBN, wave, 4, lane);
     }
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
+    const uint8_t* kt = lds + (t & 1) * 2 * TILE;
+    const uint8_t* vt = kt + TILE;
     const int kt0 = t * kDqBN;
     if (CAUSAL && kt0 > q0 + 31) continue;
 
+    // S^T = K Q^T and dP^T = V dO^T (lane owns query qrow, 16 keys per 32-key block).
     f32x16_t s[kDqBN / 32], dp[kDqBN / 32];
 #pragma unroll
-    for (int kb = 0; kb < kDqBN / 32; ++kb) {
+    for (int kb = 0; kb < kDqBN / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s[kb][i] = 0.f;
         dp[kb][i] = 0.f;
       }
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s[kb] = mfma32<T>(lds_read16B(k_lds + (kb * 32 + n) * TL::KP + 16 * c + 8 * g), qop[c], s[kb]);
-        dp[kb] = mfma32<T>(lds_read16B(v_lds + (kb * 32 + n) * TL::VP + 16 * c + 8 * g), doop[c], dp[kb]);
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int kb = 0; kb < kDqBN / 32; ++kb) {
+        const int ch = 2 * c + g;
+        const int off = (kb * 32 + n) * TL::RB + (ch ^ fk) * 16;
+        s[kb] = mfma32<T>(*(const u32x4_t*)(kt + off), qop[c], s[kb]);
+        dp[kb] = mfma32<T>(*(const u32x4_t*)(vt + off), doop[c], dp[kb]);
       }
-    }
-    const bool need_mask = (kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0);
-    u32x4_t dsop[kDqBN / 16];
+    const bool edge = (kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0);
 #pragma unroll
     for (int kb = 0; kb < kDqBN / 32; ++kb)
 #pragma unroll
@@ -186,33 +174,28 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const uint16_t* __restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int i = 8 * c2 + e;
-          float p = fast_exp2(fminf(s[kb][i] * scale_log2 - lse2, 0.f));
-          if (need_mask) {
+          float p = fast_exp2(fminf(fmaf(s[kb][i], scale_log2, -lse2), 0.f));
+          if (edge) {
             const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= Lkv || (CAUSAL && key > qrow)) p = 0.f;
+            p = key < key_lim ? p : 0.f;
           }
           ds[e] = p * (dp[kb][i] - dlt);
         }
-        dsop[kb * 2 + c2] = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]),
-                                      pack2<T>(ds[6], ds[7])};
-      }
-    // dQ^T += K^T dS^T
+        const u32x4_t dsop = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]),
+                                       pack2<T>(ds[6], ds[7])};
+        // dQ^T += K^T dS^T over keys kb*32 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}.
+        const uint8_t* krow_p = kt + (kb * 32 + 16 * c2 + trow) * TL::RB + 8 * (L16 & 1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
-#pragma unroll
-      for (int kb = 0; kb < kDqBN / 32; ++kb)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int row = kb * 32 + 16 * c2 + 4 * g + (L16 >> 2);
-          const u32x2_t lo = lds_read_tr16(k_lds + row * TL::KP + col);
-          const u32x2_t hi = lds_read_tr16(k_lds + (row + 8) * TL::KP + col);
-          acc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, dsop[kb * 2 + c2], acc[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const int ch = 4 * db + tx;
+          const u32x2_t lo = lds_read_tr16((const uint16_t*)(krow_p + (ch ^ ft) * 16));
+          const u32x2_t hi = lds_read_tr16((const uint16_t*)(krow_p + 8 * TL::RB + (ch ^ ft8) * 16));
+          acc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, dsop, acc[db]);
         }
-    }
+      }
   }
   if (row_ok) {
-    OutT* out = dq + row_off;
+    OutT* out = dq + qoff + (int64_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -223,57 +206,60 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------------
-// dK / dV
+// Stage 1: dK, dV
 // ---------------------------------------------------------------------------------
-constexpr int kKvBN = 128;  // key rows per workgroup (32 per wave)
-constexpr int kKvBM = 64;   // queries per tile
-
-template <int D>
-struct KvTile {
-  static constexpr int QP = D + 8;
-  static constexpr int CPR = D / 8;
-  static constexpr int RPP = kThreads / CPR;
-  static constexpr int PASSES = kKvBM / RPP;
-};
+// One workgroup = 8 waves x 16 key rows = 128 keys of one (b, hk). Each wave keeps K and
+// V of its 16 keys as B operands and the dK^T, dV^T accumulators in registers (16x16x32
+// matrix-core tiles keep that state at 96 registers per lane, so two waves share a SIMD),
+// and streams Q/dO tiles of 64 queries of every query head of the group.
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
+constexpr int kKvBM = 64;             // queries per tile
 
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          const float* __restrict__ lse,
-                                                          const uint16_t* __restrict__ dO,
-                                                          const float* __restrict__ delta, OutT* __restrict__ dk,
-                                                          OutT* __restrict__ dv, int Hq, int G, int Lq, int Lkv,
-                                                          int n_kblk, int n_bhk, float scale_log2, float scale) {
-  using TL = KvTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kKvBM * TL::QP];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[kKvBM * TL::QP];
-  __shared__ __attribute__((aligned(16))) float lse_lds[kKvBM];
-  __shared__ __attribute__((aligned(16))) float dl_lds[kKvBM];
+__global__ __launch_bounds__(kKvThreads, 1) void dkv_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v,
+                                                            const uint16_t* __restrict__ dO,
+                                                            const f32x2_t* __restrict__ rowstat,
+                                                            OutT* __restrict__ dk, OutT* __restrict__ dv, int Hq,
+                                                            int G, int Lq, int Lkv, int n_kblk, int n_bhk,
+                                                            int lq_pad, float scale_log2, float scale) {
+  using TL = SwzTile<D, 16>;
+  constexpr int TILE = kKvBM * TL::RB;
+  constexpr int STAT = kKvBM * 8;       // {LSE*log2e, Delta} of the tile's queries
+  constexpr int BUF = 2 * TILE + STAT;  // one buffer: Q tile, dO tile, stats
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
 
-  // Key block 0 sees the most causal queries; low block ids are dispatched first.
+  // Low block ids carry the key blocks that see the most causal queries (dispatched
+  // first). With n_bhk a multiple of 8, dispatch id % 8 == bhk % 8: each XCD keeps to
+  // its own KV groups.
   const int kblk = blockIdx.x / n_bhk;
   const int bhk = blockIdx.x - kblk * n_bhk;
   const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, g = lane >> 5;
-  const int kw0 = kblk * kKvBN + wave * 32;  // first key of this wave
-  const int krow = kw0 + n;
-  const bool key_ok = krow < Lkv;
-  const int64_t krow_off = ((int64_t)bhk * Lkv + (key_ok ? krow : 0)) * D;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int kw0 = kblk * kKvBN + wave * 16;  // first key of this wave
+  const int krow = kw0 + n16;
 
-  // K^T and V^T as B operands: lane (n, g) holds row krow, d = 16c + 8g .. +7.
-  u32x4_t kop[D / 16], vop[D / 16];
+  // K^T and V^T as B operands: lane (n16, q4) holds row krow, d = 32c + 8*q4 .. +7.
+  const int64_t kvoff = (int64_t)bhk * Lkv * D;
+  const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
+  const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
+  u32x4_t kop[D / 32], vop[D / 32];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    kop[c] = key_ok ? gload16B(k + krow_off + 16 * c + 8 * g) : (u32x4_t){0u, 0u, 0u, 0u};
-    vop[c] = key_ok ? gload16B(v + krow_off + 16 * c + 8 * g) : (u32x4_t){0u, 0u, 0u, 0u};
+  for (int c = 0; c < D / 32; ++c) {
+    const uint32_t e = (uint32_t)(krow * D + 32 * c + 8 * q4) * 2;
+    kop[c] = buf_load16(rk, e);
+    vop[c] = buf_load16(rv, e);
   }
-  f32x16_t dka[D / 32], dva[D / 32];
+  // dK^T, dV^T: block db holds d = 16*db + 4*q4 + i of key krow.
+  f32x4_t dka[D / 16], dva[D / 16];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 4; ++i) {
       dka[db][i] = 0.f;
       dva[db][i] = 0.f;
     }
@@ -281,125 +267,116 @@ __global__ __launch_bounds__(kThreads, 1) void dkv_kernel(const uint16_t* __rest
   const int q_begin = CAUSAL ? (kblk * kKvBN / kKvBM) * kKvBM : 0;
   const int ntiles = (Lq - q_begin + kKvBM - 1) / kKvBM;
   const int total = G * ntiles;  // (head, query tile) pairs, head-major
-  const int ld_row = tid / TL::CPR, ld_col = (tid % TL::CPR) * 8;
-  u32x4_t qbuf[TL::PASSES], dbuf[TL::PASSES];
-  float side = 0.f;  // threads 0..63 carry LSE*log2e, 64..127 carry Delta
-  auto fetch = [&](int it) {
+  const int L16 = lane & 15;
+  const int fa = TL::f(n16);                    // 16-byte reads: row qm*16 + n16
+  const int trow = 4 * q4 + (L16 >> 2);         // transposed reads: rows 32c' + trow (+16)
+  const int ft = TL::f(trow);
+  const int tcol = 8 * (L16 & 1);               // byte within the 16-byte chunk
+  const int tch = (L16 & 3) >> 1;               // chunk 2*db + tch
+
+  auto issue = [&](int it, uint8_t* buf) {
     const int gi = it / ntiles, t0 = q_begin + (it - gi * ntiles) * kKvBM;
-    const int64_t base = (int64_t)(b * Hq + hk * G + gi) * Lq;
-#pragma unroll
-    for (int p = 0; p < TL::PASSES; ++p) {
-      const int r = t0 + p * TL::RPP + ld_row;
-      if (r < Lq) {
-        qbuf[p] = gload16B(q + (base + r) * D + ld_col);
-        dbuf[p] = gload16B(dO + (base + r) * D + ld_col);
-      } else {
-        qbuf[p] = (u32x4_t){0u, 0u, 0u, 0u};
-        dbuf[p] = (u32x4_t){0u, 0u, 0u, 0u};
-      }
-    }
-    if (tid < 2 * kKvBM) {
-      const int r = t0 + (tid & (kKvBM - 1));
-      side = (r < Lq) ? (tid < kKvBM ? lse[base + r] * kLog2e : delta[base + r]) : 0.f;
+    const int64_t head = (int64_t)(b * Hq + hk * G + gi);
+    const rsrc_t rq = make_rsrc(q + head * Lq * D, (uint32_t)Lq * D * 2);
+    const rsrc_t rdo = make_rsrc(dO + head * Lq * D, (uint32_t)Lq * D * 2);
+    TL::template dma_fill<kKvBM>(rq, buf, t0, wave, kKvWaves, lane);
+    TL::template dma_fill<kKvBM>(rdo, buf + TILE, t0, wave, kKvWaves, lane);
+    if (wave == kKvWaves - 1 && lane < STAT / 16) {
+      const rsrc_t rs = make_rsrc(rowstat + head * lq_pad + t0, (uint32_t)(Lq - t0) * 8);
+      dma16(rs, buf + 2 * TILE, (uint32_t)(16 * lane));
     }
   };
-  const int G16 = lane >> 4, L16 = lane & 15;
-  if (total > 0) fetch(0);
+  if (total > 0) issue(0, lds);
   for (int it = 0; it < total; ++it) {
+    wait_vmem();
     __syncthreads();
-#pragma unroll
-    for (int p = 0; p < TL::PASSES; ++p) {
-      const int r = p * TL::RPP + ld_row;
-      lds_write16B(q_lds + r * TL::QP + ld_col, qbuf[p]);
-      lds_write16B(do_lds + r * TL::QP + ld_col, dbuf[p]);
-    }
-    if (tid < kKvBM)
-      lse_lds[tid] = side;
-    else if (tid < 2 * kKvBM)
-      dl_lds[tid - kKvBM] = side;
-    __syncthreads();
+    if (it + 1 < total) issue(it + 1, lds + ((it + 1) & 1) * BUF);
+    const uint8_t* qt = lds + (it & 1) * BUF;
+    const uint8_t* dt = qt + TILE;
+    const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = q_begin + (it % ntiles) * kKvBM;
-    if (it + 1 < total) fetch(it + 1);
     if (CAUSAL && t0 + kKvBM - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+    const bool edge = (t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15);
 
-    const bool need_mask = (t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 31);
-    u32x4_t pop[kKvBM / 16], dsop[kKvBM / 16];
+    // S = Q K^T and dP = dO V^T in 16-query blocks qm: lane (n16, q4) holds queries
+    // qm*16 + 4*q4 + i of key krow.
+    f32x4_t s[4], dp[4];
 #pragma unroll
-    for (int qb = 0; qb < kKvBM / 32; ++qb) {
-      f32x16_t s, dp;
+    for (int qm = 0; qm < 4; ++qm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        s[qm][i] = 0.f;
+        dp[qm][i] = 0.f;
       }
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s = mfma32<T>(lds_read16B(q_lds + (qb * 32 + n) * TL::QP + 16 * c + 8 * g), kop[c], s);
-        dp = mfma32<T>(lds_read16B(do_lds + (qb * 32 + n) * TL::QP + 16 * c + 8 * g), vop[c], dp);
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int qm = 0; qm < 4; ++qm) {
+        const int off = (qm * 16 + n16) * TL::RB + ((4 * c + q4) ^ fa) * 16;
+        s[qm] = mfma16<T>(*(const u32x4_t*)(qt + off), kop[c], s[qm]);
+        dp[qm] = mfma16<T>(*(const u32x4_t*)(dt + off), vop[c], dp[qm]);
       }
-      // Lane (n, g) holds queries qb*32 + 8*(i/4) + 4g + (i%4) of key krow.
+    // P and dS; chunk c' (32 queries) of the B operand: e = 0..3 -> block 2c', e = 4..7 -> block 2c'+1.
+    u32x4_t pop[2], dsop[2];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        float pv[8], dsv[8];
+    for (int cc = 0; cc < 2; ++cc) {
+      float pv[8], dsv[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int qi0 = qb * 32 + 16 * c2 + 8 * h + 4 * g;
-          const f32x4_t l4 = *(const f32x4_t*)(lse_lds + qi0);
-          const f32x4_t d4 = *(const f32x4_t*)(dl_lds + qi0);
+      for (int h = 0; h < 2; ++h) {
+        const int qm = 2 * cc + h;
+        const int qi0 = qm * 16 + 4 * q4;  // 4 consecutive queries
+        const f32x4_t s01 = st[qi0 / 2], s23 = st[qi0 / 2 + 1];
+        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
+        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 8 * c2 + 4 * h + j;
-            float p = fast_exp2(fminf(s[i] * scale_log2 - l4[j], 0.f));
-            if (need_mask) {
-              const int qi = t0 + qi0 + j;
-              if (qi >= Lq || (CAUSAL && krow > qi)) p = 0.f;
-            }
-            pv[4 * h + j] = p;
-            dsv[4 * h + j] = p * (dp[i] - d4[j]);
+        for (int j = 0; j < 4; ++j) {
+          float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
+          if (edge) {
+            const int qi = t0 + qi0 + j;
+            p = (qi < Lq && (!CAUSAL || krow <= qi)) ? p : 0.f;
           }
+          pv[4 * h + j] = p;
+          dsv[4 * h + j] = p * (dp[qm][j] - dl[j]);
         }
-        pop[qb * 2 + c2] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]),
-                                     pack2<T>(pv[6], pv[7])};
-        dsop[qb * 2 + c2] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]),
-                                      pack2<T>(dsv[4], dsv[5]), pack2<T>(dsv[6], dsv[7])};
       }
+      pop[cc] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]), pack2<T>(pv[6], pv[7])};
+      dsop[cc] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
+                           pack2<T>(dsv[6], dsv[7])};
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (A operands transposed out of LDS).
+    // dV^T += dO^T P and dK^T += Q^T dS: A operands transposed out of LDS, rows
+    // 32c' + 4*q4 + 0..3 (first read) and + 16 (second read), columns 16*db + L16.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
+    for (int cc = 0; cc < 2; ++cc) {
+      const int r0 = (32 * cc + trow) * TL::RB + tcol;
 #pragma unroll
-      for (int qb = 0; qb < kKvBM / 32; ++qb)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int row = qb * 32 + 16 * c2 + 4 * g + (L16 >> 2);
-          const u32x2_t dlo = lds_read_tr16(do_lds + row * TL::QP + col);
-          const u32x2_t dhi = lds_read_tr16(do_lds + (row + 8) * TL::QP + col);
-          dva[db] = mfma32<T>((u32x4_t){dlo[0], dlo[1], dhi[0], dhi[1]}, pop[qb * 2 + c2], dva[db]);
-          const u32x2_t qlo = lds_read_tr16(q_lds + row * TL::QP + col);
-          const u32x2_t qhi = lds_read_tr16(q_lds + (row + 8) * TL::QP + col);
-          dka[db] = mfma32<T>((u32x4_t){qlo[0], qlo[1], qhi[0], qhi[1]}, dsop[qb * 2 + c2], dka[db]);
-        }
+      for (int db = 0; db < D / 16; ++db) {
+        const int co = r0 + ((2 * db + tch) ^ ft) * 16;
+        const u32x2_t dlo = lds_read_tr16((const uint16_t*)(dt + co));
+        const u32x2_t dhi = lds_read_tr16((const uint16_t*)(dt + co + 16 * TL::RB));
+        dva[db] = mfma16<T>((u32x4_t){dlo[0], dlo[1], dhi[0], dhi[1]}, pop[cc], dva[db]);
+        const u32x2_t qlo = lds_read_tr16((const uint16_t*)(qt + co));
+        const u32x2_t qhi = lds_read_tr16((const uint16_t*)(qt + co + 16 * TL::RB));
+        dka[db] = mfma16<T>((u32x4_t){qlo[0], qlo[1], qhi[0], qhi[1]}, dsop[cc], dka[db]);
+      }
     }
   }
-  if (key_ok) {
+  if (krow < Lkv) {
+    const int64_t ko = kvoff + (int64_t)krow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = db * 32 + 8 * r4 + 4 * g;
-        Store4<OutT>::run(dk + krow_off + d, dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale,
-                          dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale);
-        Store4<OutT>::run(dv + krow_off + d, dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2],
-                          dva[db][4 * r4 + 3]);
-      }
+    for (int db = 0; db < D / 16; ++db) {
+      const int d = db * 16 + 4 * q4;
+      Store4<OutT>::run(dk + ko + d, dka[db][0] * scale, dka[db][1] * scale, dka[db][2] * scale, dka[db][3] * scale);
+      Store4<OutT>::run(dv + ko + d, dva[db][0], dva[db][1], dva[db][2], dva[db][3]);
+    }
   }
 }
 
 template <typename T, int D, bool C, typename OutT>
 hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                        const void* dO, void* dq, void* dk, void* dv, float* delta, float scale, int stages,
+                        const void* dO, void* dq, void* dk, void* dv, float* ws, float scale, int stages,
                         hipStream_t st) {
+  f32x2_t* rowstat = (f32x2_t*)ws;  // [B*Hq][lq_pad] {LSE*log2e, Delta}
+  const int lq_pad = (int)tiled_rowstat_stride(s.Lq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int G = (int)(s.Hq / s.Hkv);
   if (stages & kStage0) {
@@ -407,16 +384,17 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
     const int n_bh = (int)(s.B * s.Hq);
     hipLaunchKernelGGL((dq_kernel<T, D, C, OutT>), dim3(n_qblk * n_bh), dim3(kThreads), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse, (const uint16_t*)dO, (OutT*)dq,
-                       delta, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, scale);
+                       rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, lq_pad, scale_log2, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(stages & kStage1)) return hipSuccess;
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
-  hipLaunchKernelGGL((dkv_kernel<T, D, C, OutT>), dim3(n_kblk * n_bhk), dim3(kThreads), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, lse, (const uint16_t*)dO, (const float*)delta,
-                     (OutT*)dk, (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk, n_bhk, scale_log2, scale);
+  hipLaunchKernelGGL((dkv_kernel<T, D, C, OutT>), dim3(n_kblk * n_bhk), dim3(kKvThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, (const f32x2_t*)rowstat,
+                     (OutT*)dk, (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk, n_bhk, lq_pad, scale_log2,
+                     scale);
   return hipGetLastError();
 }
 

@@ -45,6 +45,16 @@ template <> __device__ __forceinline__ f32x16_t mfma32<f16_t>(u32x4_t a, u32x4_t
                                                 0, 0);
 }
 
+template <typename T> __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c);
+template <> __device__ __forceinline__ f32x4_t mfma16<bf16_t>(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x4_t mfma16<f16_t>(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                0, 0);
+}
+
 // ---- conversions --------------------------------------------------------------
 // Two fp32 values -> one dword of two 16-bit values (round to nearest even);
 // `lo` lands in bits 0..15.
@@ -84,6 +94,25 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- online softmax ------------------------------------------------------------------
+// A row's reference maximum (log2 domain) is raised only when a tile's maximum
+// exceeds it by more than this many binades, so probabilities are bounded by
+// 2^kRescaleSlack and the O rescale is skipped for most tiles.
+constexpr float kRescaleSlack = 8.0f;
+
+// ---- dispatch order ------------------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Map dispatch id i to a work id so that, within every run of 8*chunk dispatch
+// ids, XCD x receives the `chunk` consecutive work ids x*chunk .. x*chunk+chunk-1
+// (e.g. the query heads of one GQA group, which share K and V). Ids past the
+// last full run map to themselves.
+__device__ __forceinline__ int xcd_remap(int i, int n, int chunk) {
+  const int run = 8 * chunk;
+  if (chunk <= 1 || i >= (n / run) * run) return i;
+  const int base = (i / run) * run, r = i - base;
+  return base + (r & 7) * chunk + (r >> 3);
+}
+
 // ---- LDS -------------------------------------------------------------------------
 #define SDPA_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
 
@@ -94,6 +123,66 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4_t lds_read16B(const uint16_t* p) { return *(const u32x4_t*)p; }
 __device__ __forceinline__ void lds_write16B(uint16_t* p, u32x4_t v) { *(u32x4_t*)p = v; }
+
+// ---- buffer resources (range-checked loads: offsets at or past `bytes` read as zero) ----
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family buffer descriptor flags (raw, 32-bit dwords)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+// 16 bytes at byte offset `off` into registers.
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// LDS DMA: lane i copies 16 bytes from byte offset `off` to lds_base + 16*i (lds_base wave-uniform).
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0,
+                                           0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wave index as a scalar (lets the compiler keep per-wave quantities uniform).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// ---- swizzled LDS tiles ---------------------------------------------------------------
+// A tile of rows of D 16-bit elements, rows stored back to back (no padding); the 16-byte
+// chunk c of row r is stored at chunk position c ^ f(r), f(r) < D/8. The LDS has 64
+// four-byte banks (256 bytes per clock); f keeps the read patterns below conflict-free.
+// Two read geometries are supported (M = the matrix-core tile edge the kernel uses):
+//  M = 32 (32x32x16 tiles): 16-byte reads of one chunk in 16 consecutive rows, and
+//    transposed reads of an aligned group of 4 chunks in 4 consecutive rows;
+//  M = 16 (16x16x32 tiles): 16-byte reads of one chunk in 16 consecutive rows, and
+//    transposed reads of an aligned pair of chunks in 8 consecutive rows.
+template <int D, int M = 32>
+struct SwzTile {
+  static constexpr int RB = D * 2;   // row bytes
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  __device__ __forceinline__ static int f(int r) {
+    if (M == 32) {
+      if (CPR >= 16) return 4 * (r & 3) + ((r >> 2) & 3);      // 256-byte rows: one row per bank window
+      if (CPR == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);  // 128-byte rows: two rows per window
+      return (r >> 2) & 3;                                      // 64-byte rows: four rows per window
+    }
+    if (CPR >= 16) return 2 * (r & 7) + ((r >> 3) & 1);
+    if (CPR == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+    return 2 * ((r >> 2) & 1) + ((r >> 3) & 1);
+  }
+  __device__ __forceinline__ static int off(int r, int c) { return r * RB + ((c ^ f(r)) << 4); }
+  // LDS DMA of rows [g0, g0 + ROWS) of a range-checked row-major [rows, D] resource
+  // (rows past its end arrive as zeros). The `waves` waves of the workgroup split the
+  // 1 KiB slices; `w` is this wave.
+  template <int ROWS>
+  __device__ __forceinline__ static void dma_fill(rsrc_t src, uint8_t* lds, int g0, int w, int waves, int lane) {
+    constexpr int SLICES = ROWS * CPR / 64;
+    static_assert(ROWS * CPR % 64 == 0, "tile must be a whole number of 1 KiB slices");
+    for (int j = w; j < SLICES; j += waves) {
+      const int pc_lin = 64 * j + lane;
+      const int r = pc_lin / CPR, pc = pc_lin % CPR;
+      dma16(src, lds + 1024 * j, (uint32_t)(((g0 + r) * D + (pc ^ f(r)) * 8) * 2));
+    }
+  }
+};
 
 // ---- global ------------------------------------------------------------------------
 __device__ __forceinline__ u32x4_t gload16B(const void* p) { return *(const u32x4_t*)p; }

@@ -10,8 +10,10 @@
 //
 // Work decomposition: one workgroup = 4 waves = 128 query rows of one
 // (batch, query head); each wave owns 32 rows. Key/value tiles of 64 rows are
-// staged through LDS (register-prefetched one tile ahead) and shared by the 4
-// waves.
+// copied into LDS by direct buffer-to-LDS loads (range-checked, so rows past the
+// end arrive as zeros), double-buffered so that tile t+1 streams in while tile t
+// is consumed, and shared by the 4 waves. Tiles are stored unpadded with an XOR
+// swizzle of 16-byte chunks (SwzTile) that keeps both read patterns conflict-free.
 //
 // Orientation: the scores are computed transposed, S^T = K Q^T, so that in the
 // 32x32 accumulator each lane holds 16 scores of ONE query row (lanes l and
@@ -29,130 +31,122 @@ constexpr int kFwdBM = 128;  // query rows per workgroup
 constexpr int kFwdBN = 64;   // keys per tile
 constexpr int kFwdThreads = 256;
 
-template <int D>
-struct FwdTile {
-  static constexpr int KP = D + 8;    // K tile row pitch (elements): 16-byte skew, conflict-free 16-byte row reads
-  static constexpr int VP = D + 16;   // V tile row pitch: 32-byte skew, conflict-free transposed reads
-  static constexpr int CPR = D / 8;   // 16-byte chunks per row
-  static constexpr int RPP = kFwdThreads / CPR;  // rows staged per pass
-  static constexpr int PASSES = kFwdBN / RPP;
-  static_assert(PASSES >= 1 && kFwdBN % RPP == 0, "tile staging");
-};
-
 template <typename T, int D, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     OutT* __restrict__ o, float* __restrict__ lse, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
     float scale_log2) {
-  using TL = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kFwdBN * TL::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kFwdBN * TL::VP];
+  using TL = SwzTile<D>;
+  constexpr int TILE = kFwdBN * TL::RB;  // bytes of one K or V tile
+  // [buffer][K, V] tiles; buffer t & 1 holds key tile t while tile t + 1 streams into the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
 
-  int qblk = blockIdx.x / n_bh;
-  const int bh = blockIdx.x - qblk * n_bh;
-  if (CAUSAL) qblk = n_qblk - 1 - qblk;  // longest causal rows are dispatched first
+  // Work id: query block major (longest causal rows first), then (b, hq) with the
+  // G heads of a KV group adjacent and co-located on one XCD.
+  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh, G);
+  int qblk = wid / n_bh;
+  const int bh = wid - qblk * n_bh;
+  if (CAUSAL) qblk = n_qblk - 1 - qblk;
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hk = hq / G, Hkv = Hq / G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
-  const int q0 = qblk * kFwdBM + wave * 32;
+  const int q0 = qblk * kFwdBM + wave * 32;  // wave-uniform
   const int qrow = q0 + n;
 
-  const uint16_t* qh = q + (int64_t)bh * Lq * D;
   const int64_t kvoff = (int64_t)(b * Hkv + hk) * Lkv * D;
-  const uint16_t* kh = k + kvoff;
-  const uint16_t* vh = v + kvoff;
+  const rsrc_t rq = make_rsrc(q + (int64_t)bh * Lq * D, (uint32_t)Lq * D * 2);
 
-  // Q^T as the B operand: lane (n, g) holds Q[qrow][16c + 8g .. +7].
+  // Q^T as the B operand: lane (n, g) holds Q[qrow][16c + 8g .. +7] (rows past Lq read as zero).
   u32x4_t qop[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    qop[c] = (qrow < Lq) ? gload16B(qh + (int64_t)qrow * D + 16 * c + 8 * g) : (u32x4_t){0u, 0u, 0u, 0u};
+  for (int c = 0; c < D / 16; ++c) qop[c] = buf_load16(rq, (uint32_t)((qrow * D + 16 * c + 8 * g) * 2));
 
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = -INFINITY;  // running row max of the log2-domain scores
+  float m = -INFINITY;  // reference row max of the log2-domain scores (see kRescaleSlack)
   float lsum = 0.f;     // this lane's share of the running row sum
 
   const int kv_end = CAUSAL ? min(Lkv, qblk * kFwdBM + kFwdBM) : Lkv;
   const int ntiles = (kv_end + kFwdBN - 1) / kFwdBN;
+  const int key_lim = CAUSAL ? min(Lkv, qrow + 1) : Lkv;  // keys >= key_lim are masked for this row
 
-  const int ld_row = tid / TL::CPR, ld_col = (tid % TL::CPR) * 8;
-  u32x4_t kbuf[TL::PASSES], vbuf[TL::PASSES];
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int p = 0; p < TL::PASSES; ++p) {
-      const int r = t * kFwdBN + p * TL::RPP + ld_row;
-      if (r < Lkv) {
-        kbuf[p] = gload16B(kh + (int64_t)r * D + ld_col);
-        vbuf[p] = gload16B(vh + (int64_t)r * D + ld_col);
-      } else {
-        kbuf[p] = (u32x4_t){0u, 0u, 0u, 0u};
-        vbuf[p] = (u32x4_t){0u, 0u, 0u, 0u};
-      }
-    }
-  };
-
+  // Per-lane LDS offsets. K rows (16-byte reads): row kb*32 + n, chunk 2c + g.
+  // V^T (transposed 8-byte reads): row kb*32 + 16*c2 + 4g + L16/4 (+8), column chunk
+  // 4*db + 2*(G16&1) + (L16&3)/2, byte 8*(L16&1) within the chunk.
   const int G16 = lane >> 4, L16 = lane & 15;
-  fetch(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int p = 0; p < TL::PASSES; ++p) {
-      const int r = p * TL::RPP + ld_row;
-      lds_write16B(k_lds + r * TL::KP + ld_col, kbuf[p]);
-      lds_write16B(v_lds + r * TL::VP + ld_col, vbuf[p]);
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);  // next tile's global loads overlap this tile's math
+  const int fk = TL::f(n);
+  const int vrow = 4 * g + (L16 >> 2);
+  const int fv = TL::f(vrow), fv8 = TL::f(vrow + 8);  // swizzle of the two rows each transposed read pair uses
+  const int vx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
 
+  const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
+  const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
+  TL::template dma_fill<kFwdBN>(rk, lds, 0, wave, 4, lane);
+  TL::template dma_fill<kFwdBN>(rv, lds + TILE, 0, wave, 4, lane);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmem();
+    __syncthreads();  // tile t is in LDS; every wave has finished tile t - 1
+    if (t + 1 < ntiles) {
+      uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
+      TL::template dma_fill<kFwdBN>(rk, nb, (t + 1) * kFwdBN, wave, 4, lane);
+      TL::template dma_fill<kFwdBN>(rv, nb + TILE, (t + 1) * kFwdBN, wave, 4, lane);
+    }
+    const uint8_t* kt = lds + (t & 1) * 2 * TILE;
+    const uint8_t* vt = kt + TILE;
     const int kt0 = t * kFwdBN;
     if (CAUSAL && kt0 > q0 + 31) continue;  // tile entirely above this wave's diagonal
 
     // S^T = K Q^T: 32 keys x 32 queries per accumulator block.
     f32x16_t s[kFwdBN / 32];
 #pragma unroll
-    for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+    for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const u32x4_t a = lds_read16B(k_lds + (kb * 32 + n) * TL::KP + 16 * c + 8 * g);
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+        const int ch = 2 * c + g;
+        const u32x4_t a = *(const u32x4_t*)(kt + (kb * 32 + n) * TL::RB + (ch ^ fk) * 16);
         s[kb] = mfma32<T>(a, qop[c], s[kb]);
       }
-    }
 
-    // Scale into the log2 domain, mask, and take the tile's row max.
-    const bool need_mask = (kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0);
+    // Mask (only tiles that reach past the diagonal or the end), then the row max on raw scores.
+    if ((kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0)) {
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          s[kb][i] = key < key_lim ? s[kb][i] : -INFINITY;
+        }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * scale_log2;
-        if (need_mask) {
-          const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= Lkv || (CAUSAL && key > qrow)) x = -INFINITY;
-        }
-        s[kb][i] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = half_swap_max(tmax);
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
-    lsum *= alpha;
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+    tmax = half_swap_max(tmax) * scale_log2;
+    // Raise the reference max only past the slack; rescale O when any row of the wave moved.
+    const bool grow = tmax > m + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? tmax : m;
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    const float neg_m = (m == -INFINITY) ? 0.f : -m;
 
-    // P = 2^(t - m), rounded to the operand type for the P.V product.
-    u32x4_t pop[kFwdBN / 16];
+    // P = 2^(s*scale*log2e - m), rounded to the operand type, then O^T += V^T P^T.
+    // B operand chunk (kb, c2) covers keys kb*32 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}.
 #pragma unroll
     for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
@@ -160,28 +154,20 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(s[kb][8 * c2 + e] - m_use);
+          p[e] = fast_exp2(fmaf(s[kb][8 * c2 + e], scale_log2, neg_m));
           lsum += p[e];
         }
-        pop[kb * 2 + c2] = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
-                                     pack2<T>(p[6], p[7])};
-      }
-
-    // O^T += V^T P^T. B operand chunk (kb, c2) covers keys kb*32 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3};
-    // the A operand reads the same keys of V transposed.
+        const u32x4_t pop = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
+                                      pack2<T>(p[6], p[7])};
+        const uint8_t* vrow_p = vt + (kb * 32 + 16 * c2 + vrow) * TL::RB + 8 * (L16 & 1);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
-#pragma unroll
-      for (int kb = 0; kb < kFwdBN / 32; ++kb)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const int row = kb * 32 + 16 * c2 + 4 * g + (L16 >> 2);
-          const u32x2_t lo = lds_read_tr16(v_lds + row * TL::VP + col);
-          const u32x2_t hi = lds_read_tr16(v_lds + (row + 8) * TL::VP + col);
-          oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop[kb * 2 + c2], oacc[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          const int ch = 4 * db + vx;
+          const u32x2_t lo = lds_read_tr16((const uint16_t*)(vrow_p + (ch ^ fv) * 16));
+          const u32x2_t hi = lds_read_tr16((const uint16_t*)(vrow_p + 8 * TL::RB + (ch ^ fv8) * 16));
+          oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop, oacc[db]);
         }
-    }
+      }
   }
 
   const float l = half_swap_sum(lsum);

@@ -25,7 +25,9 @@ hipError_t launch_delta(const Shape& s, Dt o_dt, Dt do_dt, const void* o, const 
 hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
                             void* o, float* lse, float scale, hipStream_t st);
 
-// Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is [B*Hq*Lq] fp32 scratch.
+// Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is the workspace: per (b, hq)
+// a row of tiled_rowstat_stride(Lq) {LSE*log2e, Delta} fp32 pairs.
+inline int64_t tiled_rowstat_stride(int64_t Lq) { return (Lq + 63) / 64 * 64; }
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                             float* delta, float scale, int stages, hipStream_t st);

@@ -15,6 +15,7 @@ using sdpa::Shape;
 constexpr int64_t kMaxLen = int64_t(1) << 30;   // row indices are 32-bit inside the kernels
 constexpr int64_t kMaxRows = int64_t(1) << 31;  // B*H*L rows, and workgroup counts
 constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
 
 bool is_dtype(int d) { return d == SDPA_F32 || d == SDPA_F16 || d == SDPA_BF16; }
 
@@ -40,6 +41,9 @@ sdpa_status_t check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_
   if (rq >= kMaxRows || rk >= kMaxRows) return SDPA_ERR_SHAPE;
   if (__builtin_mul_overflow(rq, D, &eq) || __builtin_mul_overflow(rk, D, &ek)) return SDPA_ERR_SHAPE;
   if (eq > (INT64_MAX >> 3) || ek > (INT64_MAX >> 3)) return SDPA_ERR_SHAPE;
+  // One head's rows (plus a tile of slack) must be addressable with 32-bit byte offsets.
+  const int64_t esz = dtype == SDPA_F32 ? 4 : 2;
+  if ((Lq + 256) * D * esz > kMaxHeadBytes || (Lkv + 256) * D * esz > kMaxHeadBytes) return SDPA_ERR_SHAPE;
   return SDPA_OK;
 }
 
@@ -54,8 +58,11 @@ size_t delta_bytes(const Shape& s) { return align_up((size_t)(s.B * s.Hq * s.Lq)
 
 size_t ws_bytes(int backward, const Shape& s, int path) {
   if (!backward) return path == SDPA_PATH_VECTOR ? align_up(sdpa::vector_fwd_workspace(s)) : 0;
-  // The vector backward forms Delta inside its kernel; the others keep it in the workspace.
-  return path == SDPA_PATH_VECTOR ? align_up(sdpa::vector_bwd_workspace(s)) : delta_bytes(s);
+  // The vector backward forms Delta inside its kernel; the fp32 path keeps Delta and the
+  // tiled path {LSE*log2e, Delta} pairs per query row in the workspace.
+  if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_bwd_workspace(s));
+  if (path == SDPA_PATH_TILED) return align_up((size_t)(s.B * s.Hq * sdpa::tiled_rowstat_stride(s.Lq)) * 8);
+  return delta_bytes(s);
 }
 
 sdpa_status_t device_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE; }

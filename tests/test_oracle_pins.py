@@ -273,10 +273,24 @@ def test_rounding_model_reduces_to_definition_in_fp64(causal):
     np.testing.assert_allclose(oe, o, atol=1e-13)
     oe2 = emulate_forward(q, k, v, 0.25, causal, "f64", "f64", kv_block=4, kv_segment=12)
     np.testing.assert_allclose(oe2, o, atol=1e-13)
+    oe3 = emulate_forward(q, k, v, 0.25, causal, "f64", "f64", kv_block=8, slack=5.5)
+    np.testing.assert_allclose(oe3, o, atol=1e-13)
     dq, dk, dv = ref.attention_backward(q, k, v, do, 0.25, causal)
     edq, edk, edv = emulate_backward(q, k, v, do, o, lse, 0.25, causal, "f64", "f64")
     for a, b_ in ((edq, dq), (edk, dk), (edv, dv)):
         np.testing.assert_allclose(a, b_, atol=1e-12)
+
+
+def test_reference_max_slack_rule():
+    from oracle.rounding_floor import _running_max
+
+    s = np.array([[0.0, 1.0, 5.0, 2.0, 9.0, 20.0, -np.inf, 30.0]])
+    # blocks of 2: maxima 1, 5, 20, 30; slack 3: 1 -> 5 (moves, 5 > 1+3) -> 20 -> 30
+    np.testing.assert_array_equal(_running_max(s, 2, None, 3.0)[0], [1, 1, 5, 5, 20, 20, 30, 30])
+    # slack 10: 1, then 5 (not > 11) stays 1, 20 > 11 moves, 30 not > 30 stays 20
+    np.testing.assert_array_equal(_running_max(s, 2, None, 10.0)[0], [1, 1, 1, 1, 20, 20, 20, 20])
+    # slack 0 is the running max; segments restart it
+    np.testing.assert_array_equal(_running_max(s, 2, 4, 0.0)[0], [1, 1, 5, 5, 20, 20, 30, 30])
 
 
 def test_rounding_model_floor_scales_with_precision():
