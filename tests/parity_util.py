@@ -103,16 +103,16 @@ def reference_group(case, out_dtype, b, hk, backward=True):
     """
     G = case.Hq // case.Hkv
     hs = slice(hk * G, (hk + 1) * G)
-    q = case.f64("q")[b:b + 1, hs]
-    k = case.f64("k")[b:b + 1, hk:hk + 1]
-    v = case.f64("v")[b:b + 1, hk:hk + 1]
+    q = inp.as_float64(case.q[b:b + 1, hs], case.dtype)
+    k = inp.as_float64(case.k[b:b + 1, hk:hk + 1], case.dtype)
+    v = inp.as_float64(case.v[b:b + 1, hk:hk + 1], case.dtype)
     o, lse = ref.attention_forward(q, k, v, case.scale, case.is_causal)
     op = case.dtype
     pn = path_name(case)
     o_model = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, out_dtype, KV_BLOCK[pn], slack=SLACK[pn])
     out = {"o": o[0], "lse": lse[0], "o_model": o_model[0]}
     if backward:
-        do = case.f64("do")[b:b + 1, hs]
+        do = inp.as_float64(case.do[b:b + 1, hs], case.dtype)
         dq, dk, dv = ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0)
         mdq, mdk, mdv = rf.emulate_backward_group(q, k, v, do, o_model, lse, case.scale, case.is_causal, op,
                                                   out_dtype, 0, 0)
