@@ -40,7 +40,7 @@ def test_workload_full_size(wl, device):
     tol = 1e-3 * np.abs(do).max() + (0.05 if dt != "f32" else 1e-3) * np.sqrt(Lkv)
     assert np.abs(col - do).max() <= tol
     # About 2^26 score elements of fp64 oracle work (seconds on the host), at least one group.
-    n_groups = max(1, min(B * Hkv, (1 << 26) // (G * Lq * Lkv)))
+    n_groups = max(1, min(B * Hkv, 8, (1 << 26) // (G * Lq * Lkv)))
     for b, hk in _groups(case, n_groups):
         print(f"[workload] {name} oracle on group b={b} hk={hk}", flush=True)
         want = reference_group(case, dt, b, hk)
