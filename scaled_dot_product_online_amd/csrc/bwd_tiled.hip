@@ -218,7 +218,7 @@ constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
 constexpr int kKvBM = 64;             // queries per tile
 
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kKvThreads, 1) void dkv_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const uint16_t* __restrict__ dO,
@@ -268,12 +268,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_kernel(const uint16_t* __re
   const int ntiles = (Lq - q_begin + kKvBM - 1) / kKvBM;
   const int total = G * ntiles;  // (head, query tile) pairs, head-major
   const int L16 = lane & 15;
-  const int fa = TL::f(n16);                    // 16-byte reads: row qm*16 + n16
-  const int trow = 4 * q4 + (L16 >> 2);         // transposed reads: rows 32c' + trow (+16)
-  const int ft = TL::f(trow);
-  const int tcol = 8 * (L16 & 1);               // byte within the 16-byte chunk
-  const int tch = (L16 & 3) >> 1;               // chunk 2*db + tch
-
+  const int fa0 = TL::f(n16);            // 16-byte reads: row qm*16 + n16
+  const int trow = 4 * q4 + (L16 >> 2);  // transposed reads: rows 32c' + trow (+16)
+  const int ft0 = TL::f(trow);
+  const int tcol = 8 * (L16 & 1);  // byte within the 16-byte chunk
+  const int tch = (L16 & 3) >> 1;  // chunk 2*db + tch
   auto issue = [&](int it, uint8_t* buf) {
     const int gi = it / ntiles, t0 = q_begin + (it - gi * ntiles) * kKvBM;
     const int64_t head = (int64_t)(b * Hq + hk * G + gi);
@@ -286,6 +285,119 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_kernel(const uint16_t* __re
       dma16(rs, buf + 2 * TILE, (uint32_t)(16 * lane));
     }
   };
+  constexpr int NC = D / 32;       // 32-wide steps of the S / dP contraction over d
+  constexpr int NCS = 2 * (D / 32);  // stages of the dV / dK products: (c', pair of 16-wide d blocks)
+
+  // One query tile. The LDS operand reads of each stage are issued one stage ahead of the
+  // matrix-core instructions that use them; sched_fence() keeps the compiler from sinking
+  // them back next to their uses.
+  auto tile = [&](auto masked_tag, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    // Lane constants made opaque per tile, so that the compiler recomputes the LDS
+    // addresses derived from them inside the loop instead of keeping each one live.
+    int fa = fa0, ft = ft0, q4x4 = 4 * q4;
+    asm volatile("" : "+v"(fa), "+v"(ft), "+v"(q4x4));
+    // Stage a of the S / dP products: d step c = a / 2, query blocks 2*(a % 2) + 0, 1.
+    auto load_a = [&](int a, u32x4_t* qa, u32x4_t* da) {
+      const int c = a / 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int off = ((2 * (a % 2) + h) * 16 + n16) * TL::RB + ((4 * c + q4) ^ fa) * 16;
+        qa[h] = *(const u32x4_t*)(qt + off);
+        da[h] = *(const u32x4_t*)(dt + off);
+      }
+    };
+    auto load_c = [&](int si, u32x2_t* tb) {
+      const int cc = si / (D / 32), dbp = si % (D / 32);
+      const int r0 = (32 * cc + trow) * TL::RB + tcol;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int co = r0 + ((2 * (2 * dbp + e) + tch) ^ ft) * 16;
+        tb[4 * e + 0] = lds_read_tr16((const uint16_t*)(dt + co));
+        tb[4 * e + 1] = lds_read_tr16((const uint16_t*)(dt + co + 16 * TL::RB));
+        tb[4 * e + 2] = lds_read_tr16((const uint16_t*)(qt + co));
+        tb[4 * e + 3] = lds_read_tr16((const uint16_t*)(qt + co + 16 * TL::RB));
+      }
+    };
+
+    // Row statistics of this lane's queries qm*16 + 4*q4 + j.
+    f32x4_t sa[4], sb[4];
+#pragma unroll
+    for (int qm = 0; qm < 4; ++qm) {
+      const int qi0 = qm * 16 + 4 * q4;
+      sa[qm] = st[qi0 / 2];
+      sb[qm] = st[qi0 / 2 + 1];
+    }
+    u32x4_t qa[2][2], da[2][2];
+    load_a(0, qa[0], da[0]);
+    sched_fence();
+
+    // S = Q K^T and dP - Delta = dO V^T - Delta (Delta enters as the accumulator's start)
+    // in 16-query blocks qm: lane (n16, q4) holds queries qm*16 + 4*q4 + j of key krow.
+    f32x4_t s[4], dp[4];
+#pragma unroll
+    for (int qm = 0; qm < 4; ++qm) {
+      s[qm] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      dp[qm] = (f32x4_t){-sa[qm][1], -sa[qm][3], -sb[qm][1], -sb[qm][3]};
+    }
+    u32x2_t tb[2][8];
+#pragma unroll
+    for (int a = 0; a < 2 * NC; ++a) {
+      if (a + 1 < 2 * NC) load_a(a + 1, qa[(a + 1) & 1], da[(a + 1) & 1]);
+      else load_c(0, tb[0]);
+      const int c = a / 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qm = 2 * (a % 2) + h;
+        s[qm] = mfma16<T>(qa[a & 1][h], kop[c], s[qm]);
+        dp[qm] = mfma16<T>(da[a & 1][h], vop[c], dp[qm]);
+      }
+      sched_fence();
+    }
+
+    // P and dS as B operands; chunk c' (32 queries): e = 0..3 -> block 2c', e = 4..7 -> block 2c'+1.
+    u32x4_t pop[2], dsop[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qm = 2 * cc + h;
+        const float l2[4] = {sa[qm][0], sa[qm][2], sb[qm][0], sb[qm][2]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
+          if constexpr (MASKED) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, is not before key krow
+            const int u = t0 + qm * 16 + j;  // wave-uniform part
+            p = (q4x4 < Lq - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
+          }
+          pv[4 * h + j] = p;
+          dsv[4 * h + j] = p * dp[qm][j];
+        }
+      }
+      pop[cc] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]), pack2<T>(pv[6], pv[7])};
+      dsop[cc] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
+                           pack2<T>(dsv[6], dsv[7])};
+    }
+    sched_fence();
+
+    // dV^T += dO^T P and dK^T += Q^T dS: A operands transposed out of LDS, rows
+    // 32c' + 4*q4 + 0..3 (first read) and + 16 (second read), columns 16*db + L16.
+#pragma unroll
+    for (int si = 0; si < NCS; ++si) {
+      if (si + 1 < NCS) load_c(si + 1, tb[(si + 1) & 1]);
+      const int cc = si / (D / 32), dbp = si % (D / 32);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int db = 2 * dbp + e;
+        const u32x2_t* b = tb[si & 1] + 4 * e;
+        dva[db] = mfma16<T>((u32x4_t){b[0][0], b[0][1], b[1][0], b[1][1]}, pop[cc], dva[db]);
+        dka[db] = mfma16<T>((u32x4_t){b[2][0], b[2][1], b[3][0], b[3][1]}, dsop[cc], dka[db]);
+      }
+      sched_fence();
+    }
+  };
+
   if (total > 0) issue(0, lds);
   for (int it = 0; it < total; ++it) {
     wait_vmem();
@@ -296,69 +408,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void dkv_kernel(const uint16_t* __re
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = q_begin + (it % ntiles) * kKvBM;
     if (CAUSAL && t0 + kKvBM - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
-    const bool edge = (t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15);
-
-    // S = Q K^T and dP = dO V^T in 16-query blocks qm: lane (n16, q4) holds queries
-    // qm*16 + 4*q4 + i of key krow.
-    f32x4_t s[4], dp[4];
-#pragma unroll
-    for (int qm = 0; qm < 4; ++qm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[qm][i] = 0.f;
-        dp[qm][i] = 0.f;
-      }
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int qm = 0; qm < 4; ++qm) {
-        const int off = (qm * 16 + n16) * TL::RB + ((4 * c + q4) ^ fa) * 16;
-        s[qm] = mfma16<T>(*(const u32x4_t*)(qt + off), kop[c], s[qm]);
-        dp[qm] = mfma16<T>(*(const u32x4_t*)(dt + off), vop[c], dp[qm]);
-      }
-    // P and dS; chunk c' (32 queries) of the B operand: e = 0..3 -> block 2c', e = 4..7 -> block 2c'+1.
-    u32x4_t pop[2], dsop[2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int qm = 2 * cc + h;
-        const int qi0 = qm * 16 + 4 * q4;  // 4 consecutive queries
-        const f32x4_t s01 = st[qi0 / 2], s23 = st[qi0 / 2 + 1];
-        const float l2[4] = {s01[0], s01[2], s23[0], s23[2]};
-        const float dl[4] = {s01[1], s01[3], s23[1], s23[3]};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
-          if (edge) {
-            const int qi = t0 + qi0 + j;
-            p = (qi < Lq && (!CAUSAL || krow <= qi)) ? p : 0.f;
-          }
-          pv[4 * h + j] = p;
-          dsv[4 * h + j] = p * (dp[qm][j] - dl[j]);
-        }
-      }
-      pop[cc] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]), pack2<T>(pv[6], pv[7])};
-      dsop[cc] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
-                           pack2<T>(dsv[6], dsv[7])};
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS: A operands transposed out of LDS, rows
-    // 32c' + 4*q4 + 0..3 (first read) and + 16 (second read), columns 16*db + L16.
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int r0 = (32 * cc + trow) * TL::RB + tcol;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const int co = r0 + ((2 * db + tch) ^ ft) * 16;
-        const u32x2_t dlo = lds_read_tr16((const uint16_t*)(dt + co));
-        const u32x2_t dhi = lds_read_tr16((const uint16_t*)(dt + co + 16 * TL::RB));
-        dva[db] = mfma16<T>((u32x4_t){dlo[0], dlo[1], dhi[0], dhi[1]}, pop[cc], dva[db]);
-        const u32x2_t qlo = lds_read_tr16((const uint16_t*)(qt + co));
-        const u32x2_t qhi = lds_read_tr16((const uint16_t*)(qt + co + 16 * TL::RB));
-        dka[db] = mfma16<T>((u32x4_t){qlo[0], qlo[1], qhi[0], qhi[1]}, dsop[cc], dka[db]);
-      }
-    }
+    if ((t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15))  // wave-uniform
+      tile(std::true_type{}, qt, dt, st, t0);
+    else
+      tile(std::false_type{}, qt, dt, st, t0);
   }
   if (krow < Lkv) {
     const int64_t ko = kvoff + (int64_t)krow * D;

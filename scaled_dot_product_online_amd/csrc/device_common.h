@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sdpa {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -143,17 +145,23 @@ __device__ __forceinline__ void dma16(rsrc_t r, void* lds_base, uint32_t off) {
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wave index as a scalar (lets the compiler keep per-wave quantities uniform).
+// Scheduling fence: the compiler moves no instruction across it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // ---- swizzled LDS tiles ---------------------------------------------------------------
 // A tile of rows of D 16-bit elements, rows stored back to back (no padding); the 16-byte
 // chunk c of row r is stored at chunk position c ^ f(r), f(r) < D/8. The LDS has 64
-// four-byte banks (256 bytes per clock); f keeps the read patterns below conflict-free.
-// Two read geometries are supported (M = the matrix-core tile edge the kernel uses):
-//  M = 32 (32x32x16 tiles): 16-byte reads of one chunk in 16 consecutive rows, and
-//    transposed reads of an aligned group of 4 chunks in 4 consecutive rows;
-//  M = 16 (16x16x32 tiles): 16-byte reads of one chunk in 16 consecutive rows, and
-//    transposed reads of an aligned pair of chunks in 8 consecutive rows.
+// four-byte banks (256 bytes per clock). Measured on gfx950 (a lane pair that reads one
+// bank only costs a cycle when both lanes sit in the same phase), ds_read_b128 serves a
+// wave in four phases of 16 lanes, {0-3, 12-15, 20-27}, {4-11, 16-19, 28-31} and the same
+// two sets plus 32, and ds_read_b64_tr_b16 in two phases, lanes 0-31 and 32-63; f makes
+// the 16 (b128) or 32 (tr) lanes of every phase touch 64 distinct banks. Two read
+// geometries are supported (M = the matrix-core tile edge the kernel uses):
+//  M = 32 (32x32x16 tiles): lane l reads chunk 2c + l/32 of row l%32, and transposed
+//    reads of an aligned group of 4 chunks in 4 consecutive rows;
+//  M = 16 (16x16x32 tiles): lane l reads chunk 4c + l/16 of row l%16, and transposed
+//    reads of an aligned pair of chunks in 8 consecutive rows.
 template <int D, int M = 32>
 struct SwzTile {
   static constexpr int RB = D * 2;   // row bytes
@@ -164,9 +172,9 @@ struct SwzTile {
       if (CPR == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);  // 128-byte rows: two rows per window
       return (r >> 2) & 3;                                      // 64-byte rows: four rows per window
     }
-    if (CPR >= 16) return 2 * (r & 7) + ((r >> 3) & 1);
-    if (CPR == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-    return 2 * ((r >> 2) & 1) + ((r >> 3) & 1);
+    if (CPR >= 16) return 2 * (r & 7);
+    if (CPR == 8) return 2 * ((r >> 1) & 3);
+    return 2 * ((r >> 2) & 1);
   }
   __device__ __forceinline__ static int off(int r, int c) { return r * RB + ((c ^ f(r)) << 4); }
   // LDS DMA of rows [g0, g0 + ROWS) of a range-checked row-major [rows, D] resource
