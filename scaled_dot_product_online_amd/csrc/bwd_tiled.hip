@@ -125,10 +125,98 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
   const int ntiles = (kv_end + kDqBN - 1) / kDqBN;
   const int key_lim = CAUSAL ? min(Lkv, qrow + 1) : Lkv;
   const int G16 = lane >> 4, L16 = lane & 15;
-  const int fk = TL::f(n);
+  const int fk0 = TL::f(n);
   const int trow = 4 * g + (L16 >> 2);
-  const int ft = TL::f(trow), ft8 = TL::f(trow + 8);  // swizzle of the two rows each transposed read pair uses
+  const int ft0 = TL::f(trow), ft80 = TL::f(trow + 8);  // swizzle of the two rows each transposed read pair uses
   const int tx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
+  constexpr int NKB = kDqBN / 32;  // 32-key blocks per tile
+  constexpr int NC = D / 16;       // 16-wide steps of the S / dP contraction over d
+
+  // One key tile. As in the dK/dV kernel, each stage's LDS reads are issued one stage
+  // ahead of the matrix-core instructions that use them, behind scheduling fences.
+  auto tile = [&](bool masked, const uint8_t* kt, const uint8_t* vt, int kt0) {
+    // Lane constants made opaque per tile, so that the compiler rebuilds the LDS addresses
+    // derived from them inside the loop instead of keeping each one live across it.
+    // Chunk 2c + g of row n sits at (2c ^ (g ^ f(n))); chunk 4db + tx of row r at (4db ^ (tx ^ f(r))).
+    int xs = g ^ fk0, xt = tx ^ ft0, xt8 = tx ^ ft80, klim = key_lim - 4 * g, srow = n * TL::RB,
+        trow_b = trow * TL::RB + 8 * (L16 & 1);
+    asm volatile("" : "+v"(xs), "+v"(xt), "+v"(xt8), "+v"(klim), "+v"(srow), "+v"(trow_b));
+    // Stage c of the S / dP products of 32-key block kb.
+    auto load_s = [&](int kb, int c, u32x4_t* kv) {
+      const int off = kb * 32 * TL::RB + srow + ((2 * c) ^ xs) * 16;
+      kv[0] = *(const u32x4_t*)(kt + off);
+      kv[1] = *(const u32x4_t*)(vt + off);
+    };
+    // dQ stage c2 of block kb: keys kb*32 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}, all d blocks.
+    auto load_q = [&](int kb, int c2, u32x2_t* tb) {
+      const uint8_t* krow_p = kt + (kb * 32 + 16 * c2) * TL::RB + trow_b;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        tb[2 * db] = lds_read_tr16((const uint16_t*)(krow_p + ((4 * db) ^ xt) * 16));
+        tb[2 * db + 1] = lds_read_tr16((const uint16_t*)(krow_p + 8 * TL::RB + ((4 * db) ^ xt8) * 16));
+      }
+    };
+
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T for keys kb*32 .. +31 (lane owns query qrow and 16
+      // of the keys).
+      u32x4_t kv[2][2];
+      load_s(kb, 0, kv[0]);
+      sched_fence();
+      f32x16_t s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+      u32x2_t tb[2][D / 16];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (c + 1 < NC) load_s(kb, c + 1, kv[(c + 1) & 1]);
+        else load_q(kb, 0, tb[0]);
+        s = mfma32<T>(kv[c & 1][0], qop[c], s);
+        dp = mfma32<T>(kv[c & 1][1], doop[c], dp);
+        sched_fence();
+      }
+      // dS^T as B operands, one per 16-key half c2. Only the softmax is duplicated for
+      // the masked case (a wave-uniform branch), so both paths share the same registers.
+      u32x4_t dsop[2];
+      auto softmax = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          float ds[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = 8 * c2 + e;
+            float p = fast_exp2(fminf(fmaf(s[i], scale_log2, -lse2), 0.f));
+            if constexpr (MASKED)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
+              p = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) < klim ? p : 0.f;
+            ds[e] = p * (dp[i] - dlt);
+          }
+          dsop[c2] = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]),
+                               pack2<T>(ds[6], ds[7])};
+        }
+      };
+      if (masked)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
+      sched_fence();
+      // dQ^T += K^T dS^T.
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        if (c2 == 0) load_q(kb, 1, tb[1]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x2_t lo = tb[c2][2 * db], hi = tb[c2][2 * db + 1];
+          acc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, dsop[c2], acc[db]);
+        }
+        sched_fence();
+      }
+    }
+  };
 
   const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
   const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
@@ -146,53 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
     const uint8_t* vt = kt + TILE;
     const int kt0 = t * kDqBN;
     if (CAUSAL && kt0 > q0 + 31) continue;
-
-    // S^T = K Q^T and dP^T = V dO^T (lane owns query qrow, 16 keys per 32-key block).
-    f32x16_t s[kDqBN / 32], dp[kDqBN / 32];
-#pragma unroll
-    for (int kb = 0; kb < kDqBN / 32; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[kb][i] = 0.f;
-        dp[kb][i] = 0.f;
-      }
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int kb = 0; kb < kDqBN / 32; ++kb) {
-        const int ch = 2 * c + g;
-        const int off = (kb * 32 + n) * TL::RB + (ch ^ fk) * 16;
-        s[kb] = mfma32<T>(*(const u32x4_t*)(kt + off), qop[c], s[kb]);
-        dp[kb] = mfma32<T>(*(const u32x4_t*)(vt + off), doop[c], dp[kb]);
-      }
-    const bool edge = (kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0);
-#pragma unroll
-    for (int kb = 0; kb < kDqBN / 32; ++kb)
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        float ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * c2 + e;
-          float p = fast_exp2(fminf(fmaf(s[kb][i], scale_log2, -lse2), 0.f));
-          if (edge) {
-            const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            p = key < key_lim ? p : 0.f;
-          }
-          ds[e] = p * (dp[kb][i] - dlt);
-        }
-        const u32x4_t dsop = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]),
-                                       pack2<T>(ds[6], ds[7])};
-        // dQ^T += K^T dS^T over keys kb*32 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}.
-        const uint8_t* krow_p = kt + (kb * 32 + 16 * c2 + trow) * TL::RB + 8 * (L16 & 1);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int ch = 4 * db + tx;
-          const u32x2_t lo = lds_read_tr16((const uint16_t*)(krow_p + (ch ^ ft) * 16));
-          const u32x2_t hi = lds_read_tr16((const uint16_t*)(krow_p + 8 * TL::RB + (ch ^ ft8) * 16));
-          acc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, dsop, acc[db]);
-        }
-      }
+    tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0), kt, vt, kt0);  // wave-uniform flag
   }
   if (row_ok) {
     OutT* out = dq + qoff + (int64_t)qrow * D;
@@ -291,8 +333,7 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
   // One query tile. The LDS operand reads of each stage are issued one stage ahead of the
   // matrix-core instructions that use them; sched_fence() keeps the compiler from sinking
   // them back next to their uses.
-  auto tile = [&](auto masked_tag, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  auto tile = [&](bool masked, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0) {
     // Lane constants made opaque per tile, so that the compiler recomputes the LDS
     // addresses derived from them inside the loop instead of keeping each one live.
     int fa = fa0, ft = ft0, q4x4 = 4 * q4;
@@ -356,29 +397,39 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
     }
 
     // P and dS as B operands; chunk c' (32 queries): e = 0..3 -> block 2c', e = 4..7 -> block 2c'+1.
+    // Only the softmax is duplicated for the masked case (a wave-uniform branch), so
+    // both paths share the same registers.
     u32x4_t pop[2], dsop[2];
+    auto softmax = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      float pv[8], dsv[8];
+      for (int cc = 0; cc < 2; ++cc) {
+        float pv[8], dsv[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int qm = 2 * cc + h;
-        const float l2[4] = {sa[qm][0], sa[qm][2], sb[qm][0], sb[qm][2]};
+        for (int h = 0; h < 2; ++h) {
+          const int qm = 2 * cc + h;
+          const float l2[4] = {sa[qm][0], sa[qm][2], sb[qm][0], sb[qm][2]};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
-          if constexpr (MASKED) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, is not before key krow
-            const int u = t0 + qm * 16 + j;  // wave-uniform part
-            p = (q4x4 < Lq - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
+          for (int j = 0; j < 4; ++j) {
+            float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
+            if constexpr (MASKED) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, is not before key krow
+              const int u = t0 + qm * 16 + j;  // wave-uniform part
+              p = (q4x4 < Lq - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
+            }
+            pv[4 * h + j] = p;
+            dsv[4 * h + j] = p * dp[qm][j];
           }
-          pv[4 * h + j] = p;
-          dsv[4 * h + j] = p * dp[qm][j];
         }
+        pop[cc] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]),
+                            pack2<T>(pv[6], pv[7])};
+        dsop[cc] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
+                             pack2<T>(dsv[6], dsv[7])};
       }
-      pop[cc] = (u32x4_t){pack2<T>(pv[0], pv[1]), pack2<T>(pv[2], pv[3]), pack2<T>(pv[4], pv[5]), pack2<T>(pv[6], pv[7])};
-      dsop[cc] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
-                           pack2<T>(dsv[6], dsv[7])};
-    }
+    };
+    if (masked)
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
     sched_fence();
 
     // dV^T += dO^T P and dK^T += Q^T dS: A operands transposed out of LDS, rows
@@ -408,10 +459,7 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = q_begin + (it % ntiles) * kKvBM;
     if (CAUSAL && t0 + kKvBM - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
-    if ((t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15))  // wave-uniform
-      tile(std::true_type{}, qt, dt, st, t0);
-    else
-      tile(std::false_type{}, qt, dt, st, t0);
+    tile((t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15), qt, dt, st, t0);  // wave-uniform flag
   }
   if (krow < Lkv) {
     const int64_t ko = kvoff + (int64_t)krow * D;
