@@ -234,8 +234,9 @@ def config_of(name):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the (b, kv-head) groups are "
-              "independent; see DESIGN.md for how it would shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (the (b, kv-head) groups are "
+              "independent, so a run would shard them across GPUs with no communication). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -308,7 +308,11 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
 
   const int q_begin = CAUSAL ? (kblk * kKvBN / kKvBM) * kKvBM : 0;
   const int ntiles = (Lq - q_begin + kKvBM - 1) / kKvBM;
-  const int total = G * ntiles;  // (head, query tile) pairs, head-major
+  // (head, query tile) pairs, query tiles from the last one backward and the G heads of
+  // each tile together: every workgroup of a KV group starts at the same (last) tile, so
+  // the workgroups that run at once stream the same Q / dO tiles and share them in L2.
+  const int total = G * ntiles;
+  auto tile_of = [&](int it) { return q_begin + (ntiles - 1 - it / G) * kKvBM; };
   const int L16 = lane & 15;
   const int fa0 = TL::f(n16);            // 16-byte reads: row qm*16 + n16
   const int trow = 4 * q4 + (L16 >> 2);  // transposed reads: rows 32c' + trow (+16)
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
   const int tcol = 8 * (L16 & 1);  // byte within the 16-byte chunk
   const int tch = (L16 & 3) >> 1;  // chunk 2*db + tch
   auto issue = [&](int it, uint8_t* buf) {
-    const int gi = it / ntiles, t0 = q_begin + (it - gi * ntiles) * kKvBM;
+    const int gi = it % G, t0 = tile_of(it);
     const int64_t head = (int64_t)(b * Hq + hk * G + gi);
     const rsrc_t rq = make_rsrc(q + head * Lq * D, (uint32_t)Lq * D * 2);
     const rsrc_t rdo = make_rsrc(dO + head * Lq * D, (uint32_t)Lq * D * 2);
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
     const uint8_t* qt = lds + (it & 1) * BUF;
     const uint8_t* dt = qt + TILE;
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
-    const int t0 = q_begin + (it % ntiles) * kKvBM;
+    const int t0 = tile_of(it);
     if (CAUSAL && t0 + kKvBM - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
     tile((t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15), qt, dt, st, t0);  // wave-uniform flag
   }
