@@ -138,13 +138,26 @@ __device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 // LDS DMA: lane i copies 16 bytes from byte offset `off` to lds_base + 16*i (lds_base wave-uniform).
+// Cache policy of a buffer load: kCacheDefault, or kCacheStream (non-temporal) for data
+// read exactly once, which measured 7.1-7.3 TB/s against 5.9-6.1 TB/s for default loads
+// in a pure read stream on MI355X.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
+template <int CPOL = kCacheDefault>
 __device__ __forceinline__ void dma16(rsrc_t r, void* lds_base, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)off, 0, 0,
-                                           0);
+                                           CPOL);
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wave index as a scalar (lets the compiler keep per-wave quantities uniform).
+// Orders the LDS accesses of one wave: everything before completes and is visible to
+// the wave's lanes before anything after it (a wave-scope fence around a wave barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 // Scheduling fence: the compiler moves no instruction across it.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -180,14 +193,14 @@ struct SwzTile {
   // LDS DMA of rows [g0, g0 + ROWS) of a range-checked row-major [rows, D] resource
   // (rows past its end arrive as zeros). The `waves` waves of the workgroup split the
   // 1 KiB slices; `w` is this wave.
-  template <int ROWS>
+  template <int ROWS, int CPOL = kCacheDefault>
   __device__ __forceinline__ static void dma_fill(rsrc_t src, uint8_t* lds, int g0, int w, int waves, int lane) {
     constexpr int SLICES = ROWS * CPR / 64;
     static_assert(ROWS * CPR % 64 == 0, "tile must be a whole number of 1 KiB slices");
     for (int j = w; j < SLICES; j += waves) {
       const int pc_lin = 64 * j + lane;
       const int r = pc_lin / CPR, pc = pc_lin % CPR;
-      dma16(src, lds + 1024 * j, (uint32_t)(((g0 + r) * D + (pc ^ f(r)) * 8) * 2));
+      dma16<CPOL>(src, lds + 1024 * j, (uint32_t)(((g0 + r) * D + (pc ^ f(r)) * 8) * 2));
     }
   }
 };

@@ -88,18 +88,40 @@ __device__ __forceinline__ void wave_store(uint16_t* lds, const u32x4_t* buf, in
 // ---------------------------------------------------------------------------------
 // Forward split
 // ---------------------------------------------------------------------------------
+// One workgroup of 4 waves per CU (the plan sizes the grid to the CU count). Each wave
+// streams its own contiguous key segment in 32-key steps: K and V tiles go straight from
+// HBM into a two-slot LDS ring owned by the wave (direct buffer-to-LDS loads with the
+// non-temporal policy: K and V are read exactly once), so the wave only waits on its own
+// loads and never on the other waves until the final merge. The tiles use the same
+// swizzled layout and read patterns as the tiled forward.
+constexpr int kVecKeys = 32;  // keys per step
+constexpr int kVecRing = 2;   // LDS slots per wave
+
+SplitPlan plan_fwd(const Shape& s) {
+  const int64_t groups = s.B * s.Hkv * ((s.Hq / s.Hkv * s.Lq + 31) / 32);
+  const int64_t unit = kWaves * kVecKeys;  // one step per wave
+  const int64_t units = (s.Lkv + unit - 1) / unit;
+  int64_t want = (256 + groups - 1) / groups;  // about one workgroup per CU
+  if (want < 1) want = 1;
+  if (want > units) want = units;
+  const int64_t len = ((s.Lkv + want - 1) / want + unit - 1) / unit * unit;
+  return SplitPlan{(int)((s.Lkv + len - 1) / len), len};
+}
+
 template <typename T, int D, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void vec_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, OutT* __restrict__ o,
                                                               float* __restrict__ lse, float* __restrict__ part_o,
                                                               float* __restrict__ part_ml, int Hq, int G, int Lq,
                                                               int Lkv, int nsplit, int split_len, int n_rb,
                                                               int64_t total_rows, float scale_log2) {
-  using TL = VecTile<D>;
-  constexpr int WAVE_LDS = 2 * kTileKeys * TL::P;  // K and V tile of one wave
-  static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS * 2, "merge scratch must fit in the tile LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * WAVE_LDS];
+  using TL = SwzTile<D>;
+  constexpr int TILE = kVecKeys * TL::RB;         // bytes of one K or V tile
+  constexpr int WAVE_LDS = kVecRing * 2 * TILE;   // [slot][K, V]
+  constexpr int NDMA = 2 * kVecKeys * TL::CPR / 64;  // buffer-to-LDS loads per step (K and V)
+  static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS, "merge scratch must fit in the tile LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kWaves * WAVE_LDS];
   __shared__ float mrg_m[kWaves][32];
   __shared__ float mrg_l[kWaves][32];
 
@@ -107,60 +129,76 @@ __global__ __launch_bounds__(kThreads, 2) void vec_fwd_kernel(const uint16_t* __
   const int rb = (blockIdx.x / nsplit) % n_rb;
   const int bhk = blockIdx.x / (nsplit * n_rb);
   const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
   const int rows = G * Lq;
-  const int r = rb * 32 + n;  // packed row of this lane
-  const bool row_ok = r < rows;
   const int64_t row0 = (int64_t)b * Hq * Lq + (int64_t)hk * G * Lq;  // first packed row of the group
   const int64_t kv0 = (int64_t)bhk * Lkv;
 
+  // Q^T as the B operand: lane (n, g) holds packed row rb*32 + n, d = 16c + 8g .. +7
+  // (rows past the group's G*Lq read as zero).
+  const rsrc_t rq = make_rsrc(q + (row0 + rb * 32) * D, (uint32_t)max(0, rows - rb * 32) * D * 2);
   u32x4_t qop[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    qop[c] = row_ok ? gload16B(q + (row0 + r) * D + 16 * c + 8 * g) : (u32x4_t){0u, 0u, 0u, 0u};
+  for (int c = 0; c < D / 16; ++c) qop[c] = buf_load16(rq, (uint32_t)((n * D + 16 * c + 8 * g) * 2));
 
-  // This wave's contiguous key segment.
+  // This wave's contiguous key segment [kb0, kb1).
   const int seg = split_len / kWaves;
   const int kb0 = split * split_len + wave * seg;
   const int kb1 = min(kb0 + seg, Lkv);
-  const int steps = seg / kTileKeys;
+  const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
 
-  uint16_t* k_lds = lds + wave * WAVE_LDS;
-  uint16_t* v_lds = k_lds + kTileKeys * TL::P;
+  uint8_t* my = lds + wave * WAVE_LDS;
+  const rsrc_t rk = make_rsrc(k + kv0 * D, (uint32_t)Lkv * D * 2);
+  const rsrc_t rv = make_rsrc(v + kv0 * D, (uint32_t)Lkv * D * 2);
+  auto fill = [&](int st) {
+    uint8_t* slot = my + (st % kVecRing) * 2 * TILE;
+    TL::template dma_fill<kVecKeys, kCacheStream>(rk, slot, kb0 + st * kVecKeys, 0, 1, lane);
+    TL::template dma_fill<kVecKeys, kCacheStream>(rv, slot + TILE, kb0 + st * kVecKeys, 0, 1, lane);
+  };
+
+  const int G16 = lane >> 4, L16 = lane & 15;
+  const int vrow = 4 * g + (L16 >> 2);
+  const int vx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
+  const int xk = g ^ TL::f(n), xv = vx ^ TL::f(vrow), xv8 = vx ^ TL::f(vrow + 8);
+  const int srow = n * TL::RB, vrow_b = vrow * TL::RB + 8 * (L16 & 1);
+
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
-  u32x4_t kbuf[TL::LOADS], vbuf[TL::LOADS];
-  wave_fetch<D>(kbuf, k + kv0 * D, kb0, kb1, lane);
-  wave_fetch<D>(vbuf, v + kv0 * D, kb0, kb1, lane);
-  const int G16 = lane >> 4, L16 = lane & 15;
+
+  if (steps > 0) fill(0);
   for (int st = 0; st < steps; ++st) {
-    __syncthreads();  // every wave has finished reading its previous tile
-    wave_store<D>(k_lds, kbuf, lane);
-    wave_store<D>(v_lds, vbuf, lane);
-    __syncthreads();
-    const int t0 = kb0 + st * kTileKeys;
     if (st + 1 < steps) {
-      wave_fetch<D>(kbuf, k + kv0 * D, t0 + kTileKeys, kb1, lane);
-      wave_fetch<D>(vbuf, v + kv0 * D, t0 + kTileKeys, kb1, lane);
+      fill(st + 1);  // the slot of step st - 1: this wave's reads of it have completed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");  // step st has landed
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    if (t0 >= kb1) continue;  // ragged tail: nothing left in this wave's segment
+    const uint8_t* kt = my + (st % kVecRing) * 2 * TILE;
+    const uint8_t* vt = kt + TILE;
+    const int t0 = kb0 + st * kVecKeys;
+
+    // S^T = K Q^T: lane holds keys t0 + 8*(i/4) + 4g + i%4 of packed row n.
     f32x16_t s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) s = mfma32<T>(lds_read16B(k_lds + n * TL::P + 16 * c + 8 * g), qop[c], s);
+    for (int c = 0; c < D / 16; ++c)
+      s = mfma32<T>(*(const u32x4_t*)(kt + srow + ((2 * c) ^ xk) * 16), qop[c], s);
+    if (t0 + kVecKeys > kb1) {  // wave-uniform: the segment ends inside this step
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (t0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kb1) s[i] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float x = s[i] * scale_log2;
-      if (t0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kb1) x = -INFINITY;
-      s[i] = x;
-      tmax = fmaxf(tmax, x);
+      s[i] *= scale_log2;
+      tmax = fmaxf(tmax, s[i]);
     }
     tmax = half_swap_max(tmax);
     const float m_new = fmaxf(m, tmax);
@@ -183,23 +221,24 @@ __global__ __launch_bounds__(kThreads, 2) void vec_fwd_kernel(const uint16_t* __
       }
       pop[c2] = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]), pack2<T>(p[6], p[7])};
     }
+    // O^T += V^T P^T; B operand chunk c2 covers keys t0 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const uint8_t* vb = vt + 16 * c2 * TL::RB + vrow_b;
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const int row = 16 * c2 + 4 * g + (L16 >> 2);
-        const u32x2_t lo = lds_read_tr16(v_lds + row * TL::P + col);
-        const u32x2_t hi = lds_read_tr16(v_lds + (row + 8) * TL::P + col);
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2_t lo = lds_read_tr16((const uint16_t*)(vb + ((4 * db) ^ xv) * 16));
+        const u32x2_t hi = lds_read_tr16((const uint16_t*)(vb + 8 * TL::RB + ((4 * db) ^ xv8) * 16));
         oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop[c2], oacc[db]);
       }
     }
   }
   const float l = half_swap_sum(lsum);
 
-  // Merge the 4 waves: scratch O_w (fp32, [32 rows][D]) reuses the tile LDS.
+  // Merge the 4 waves: scratch O_w (fp32, [32 rows][D]) reuses the tile LDS. Every wave's
+  // loads have landed (vmcnt(0) on its last step) before the barrier.
   __syncthreads();
-  float* mrg_o = (float*)lds;  // kWaves * 32 * D floats <= kWaves * WAVE_LDS * 2 bytes
+  float* mrg_o = (float*)lds;
   if (g == 0) {
     mrg_m[wave][n] = m;
     mrg_l[wave][n] = l;
@@ -507,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __
 template <typename T, int D, typename OutT>
 hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse, float scale,
                      void* ws, hipStream_t st) {
-  const SplitPlan pl = plan(s);
+  const SplitPlan pl = plan_fwd(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int n_rb = (int)((G * s.Lq + 31) / 32);
   const int64_t tr = rows_total(s);
@@ -553,7 +592,7 @@ hipError_t bwd_typed(const Shape& s, const void* q, const void* k, const void* v
 int vector_num_splits(const Shape& s) { return plan(s).nsplit; }
 
 size_t vector_fwd_workspace(const Shape& s) {
-  const SplitPlan pl = plan(s);
+  const SplitPlan pl = plan_fwd(s);
   if (pl.nsplit == 1) return 0;
   return (size_t)pl.nsplit * (size_t)rows_total(s) * (size_t)(s.D + 2) * sizeof(float);
 }
