@@ -111,6 +111,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
     }
   }
   const float dlt = half_swap_sum(dpart);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) settle(qop[c]);
   const bool row_ok = qrow < Lq;
   const float lse2 = row_ok ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
   if (row_ok && g == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, dlt};
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
     }
   };
 
-  const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
-  const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
+  const srd_t rk = make_srd(k + kvoff, (uint32_t)Lkv * D * 2);
+  const srd_t rv = make_srd(v + kvoff, (uint32_t)Lkv * D * 2);
   TL::template dma_fill<kDqBN>(rk, lds, 0, wave, 4, lane);
   TL::template dma_fill<kDqBN>(rv, lds + TILE, 0, wave, 4, lane);
   for (int t = 0; t < ntiles; ++t) {
@@ -296,6 +298,11 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
     kop[c] = buf_load16(rk, e);
     vop[c] = buf_load16(rv, e);
   }
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    settle(kop[c]);
+    settle(vop[c]);
+  }
   // dK^T, dV^T: block db holds d = 16*db + 4*q4 + i of key krow.
   f32x4_t dka[D / 16], dva[D / 16];
 #pragma unroll
@@ -322,12 +329,12 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
   auto issue = [&](int it, uint8_t* buf) {
     const int gi = it % G, t0 = tile_of(it);
     const int64_t head = (int64_t)(b * Hq + hk * G + gi);
-    const rsrc_t rq = make_rsrc(q + head * Lq * D, (uint32_t)Lq * D * 2);
-    const rsrc_t rdo = make_rsrc(dO + head * Lq * D, (uint32_t)Lq * D * 2);
+    const srd_t rq = make_srd(q + head * Lq * D, (uint32_t)Lq * D * 2);
+    const srd_t rdo = make_srd(dO + head * Lq * D, (uint32_t)Lq * D * 2);
     TL::template dma_fill<kKvBM>(rq, buf, t0, wave, kKvWaves, lane);
     TL::template dma_fill<kKvBM>(rdo, buf + TILE, t0, wave, kKvWaves, lane);
     if (wave == kKvWaves - 1 && lane < STAT / 16) {
-      const rsrc_t rs = make_rsrc(rowstat + head * lq_pad + t0, (uint32_t)(Lq - t0) * 8);
+      const srd_t rs = make_srd(rowstat + head * lq_pad + t0, (uint32_t)(Lq - t0) * 8);
       dma16(rs, buf + 2 * TILE, (uint32_t)(16 * lane));
     }
   };

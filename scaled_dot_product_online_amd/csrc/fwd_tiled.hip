@@ -61,6 +61,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
   u32x4_t qop[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) qop[c] = buf_load16(rq, (uint32_t)((qrow * D + 16 * c + 8 * g) * 2));
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) settle(qop[c]);
 
   f32x16_t oacc[D / 32];
 #pragma unroll
@@ -83,8 +85,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
   const int fv = TL::f(vrow), fv8 = TL::f(vrow + 8);  // swizzle of the two rows each transposed read pair uses
   const int vx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
 
-  const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
-  const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
+  const srd_t rk = make_srd(k + kvoff, (uint32_t)Lkv * D * 2);
+  const srd_t rv = make_srd(v + kvoff, (uint32_t)Lkv * D * 2);
   TL::template dma_fill<kFwdBN>(rk, lds, 0, wave, 4, lane);
   TL::template dma_fill<kFwdBN>(rv, lds + TILE, 0, wave, 4, lane);
   for (int t = 0; t < ntiles; ++t) {

@@ -32,58 +32,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kTileKeys = 32;            // keys per wave per step
-constexpr int kStepKeys = kWaves * kTileKeys;
-constexpr int kTargetBlocks = 1024;      // ~4 workgroups per CU on 256 CUs
 
 struct SplitPlan {
   int nsplit;
-  int64_t split_len;  // keys per split, a multiple of kStepKeys
+  int64_t split_len;  // keys per split, a multiple of kWaves * kVecKeys
 };
-
-SplitPlan plan(const Shape& s) {
-  const int64_t groups = s.B * s.Hkv;
-  const int64_t steps = (s.Lkv + kStepKeys - 1) / kStepKeys;
-  int64_t want = (kTargetBlocks + groups - 1) / groups;
-  if (want < 1) want = 1;
-  if (want > steps) want = steps;
-  const int64_t len = ((s.Lkv + want - 1) / want + kStepKeys - 1) / kStepKeys * kStepKeys;
-  return SplitPlan{(int)((s.Lkv + len - 1) / len), len};
-}
 
 int64_t rows_total(const Shape& s) { return s.B * s.Hq * s.Lq; }
-
-template <int D>
-struct VecTile {
-  static constexpr int P = D + 8;           // K/V/Q/dO tile row pitch (elements)
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int LPW = 64 / CPR;      // rows per wave-wide load
-  static constexpr int LOADS = kTileKeys / LPW;
-  static constexpr int DSP = 32 + 16;       // dS^T scratch pitch
-};
-
-// Load rows [r0, r0+32) x D of a row-major [.., D] matrix (rows >= rmax are zero),
-// one 16-byte chunk per lane per load; consecutive lanes read consecutive chunks.
-template <int D>
-__device__ __forceinline__ void wave_fetch(u32x4_t* buf, const uint16_t* base, int64_t r0, int64_t rmax, int lane) {
-  using TL = VecTile<D>;
-#pragma unroll
-  for (int p = 0; p < TL::LOADS; ++p) {
-    const int r = p * TL::LPW + lane / TL::CPR;
-    const int c = (lane % TL::CPR) * 8;
-    buf[p] = (r0 + r < rmax) ? gload16B(base + (r0 + r) * D + c) : (u32x4_t){0u, 0u, 0u, 0u};
-  }
-}
-template <int D>
-__device__ __forceinline__ void wave_store(uint16_t* lds, const u32x4_t* buf, int lane) {
-  using TL = VecTile<D>;
-#pragma unroll
-  for (int p = 0; p < TL::LOADS; ++p) {
-    const int r = p * TL::LPW + lane / TL::CPR;
-    const int c = (lane % TL::CPR) * 8;
-    lds_write16B(lds + r * TL::P + c, buf[p]);
-  }
-}
 
 // ---------------------------------------------------------------------------------
 // Forward split
@@ -97,7 +52,7 @@ __device__ __forceinline__ void wave_store(uint16_t* lds, const u32x4_t* buf, in
 constexpr int kVecKeys = 32;  // keys per step
 constexpr int kVecRing = 2;   // LDS slots per wave
 
-SplitPlan plan_fwd(const Shape& s) {
+SplitPlan plan(const Shape& s) {
   const int64_t groups = s.B * s.Hkv * ((s.Hq / s.Hkv * s.Lq + 31) / 32);
   const int64_t unit = kWaves * kVecKeys;  // one step per wave
   const int64_t units = (s.Lkv + unit - 1) / unit;
@@ -141,6 +96,8 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
   u32x4_t qop[D / 16];
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) qop[c] = buf_load16(rq, (uint32_t)((n * D + 16 * c + 8 * g) * 2));
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) settle(qop[c]);
 
   // This wave's contiguous key segment [kb0, kb1).
   const int seg = split_len / kWaves;
@@ -149,12 +106,12 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
   const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
 
   uint8_t* my = lds + wave * WAVE_LDS;
-  const rsrc_t rk = make_rsrc(k + kv0 * D, (uint32_t)Lkv * D * 2);
-  const rsrc_t rv = make_rsrc(v + kv0 * D, (uint32_t)Lkv * D * 2);
+  const srd_t rk = make_srd(k + kv0 * D, (uint32_t)Lkv * D * 2);
+  const srd_t rv = make_srd(v + kv0 * D, (uint32_t)Lkv * D * 2);
   auto fill = [&](int st) {
     uint8_t* slot = my + (st % kVecRing) * 2 * TILE;
-    TL::template dma_fill<kVecKeys, kCacheStream>(rk, slot, kb0 + st * kVecKeys, 0, 1, lane);
-    TL::template dma_fill<kVecKeys, kCacheStream>(rv, slot + TILE, kb0 + st * kVecKeys, 0, 1, lane);
+    TL::template dma_fill<kVecKeys, kCacheStream, false>(rk, slot, kb0 + st * kVecKeys, 0, 1, lane);
+    TL::template dma_fill<kVecKeys, kCacheStream, false>(rv, slot + TILE, kb0 + st * kVecKeys, 0, 1, lane);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -334,6 +291,11 @@ __global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __re
 // ---------------------------------------------------------------------------------
 // Backward split
 // ---------------------------------------------------------------------------------
+// Same streaming layout as the forward: one workgroup of 4 waves per CU, each wave with
+// its own key segment and a two-slot LDS ring of K and V tiles fed by non-temporal
+// buffer-to-LDS loads. Q and dO of the group's 32 packed rows are staged once in
+// swizzled tiles; every LDS read uses the conflict-free patterns of the tiled forward
+// (16-byte rows for the S / dP operands, transposed reads for Q^T, dO^T and K^T).
 template <typename T, int D, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
@@ -345,35 +307,35 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
                                                               int Hq, int G, int Lq, int Lkv, int nsplit,
                                                               int split_len, int64_t total_rows, float scale_log2,
                                                               float scale) {
-  using TL = VecTile<D>;
-  constexpr int WAVE_LDS = 2 * kTileKeys * TL::P + kTileKeys * TL::DSP;
-  static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS * 2, "dQ reduction scratch must fit in the tile LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kWaves * WAVE_LDS];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[32 * TL::P];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[32 * TL::P];
+  using TL = SwzTile<D>;
+  constexpr int TILE = kVecKeys * TL::RB;        // bytes of one 32-row tile
+  constexpr int WAVE_LDS = kVecRing * 2 * TILE;  // [slot][K, V]
+  constexpr int NDMA = 2 * kVecKeys * TL::CPR / 64;
+  constexpr int DSP = 32 + 16;                   // dS^T scratch pitch (elements)
+  static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS, "dQ reduction scratch must fit in the ring LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kWaves * WAVE_LDS];
+  __shared__ __attribute__((aligned(1024))) uint8_t qd_lds[2 * TILE];  // Q tile, dO tile
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kWaves][32 * DSP];
   __shared__ __attribute__((aligned(16))) float lse_lds[32];
   __shared__ __attribute__((aligned(16))) float dl_lds[32];
 
   const int split = blockIdx.x % nsplit;
   const int bhk = blockIdx.x / nsplit;
   const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int n = lane & 31, g = lane >> 5;
   const int rows = G * Lq;
   const int64_t row0 = (int64_t)b * Hq * Lq + (int64_t)hk * G * Lq;
   const int64_t kv0 = (int64_t)bhk * Lkv;
 
-  // Stage Q and dO of the group's rows; Delta and LSE*log2e per row.
+  // Stage Q and dO of the group's rows (rows past G*Lq arrive as zeros); Delta and
+  // LSE*log2e per row.
   {
-    constexpr int CPR = D / 8;
-    for (int e = tid; e < 32 * CPR; e += kThreads) {
-      const int r = e / CPR, c = (e % CPR) * 8;
-      const bool ok = r < rows;
-      lds_write16B(q_lds + r * TL::P + c, ok ? gload16B(q + (row0 + r) * D + c) : (u32x4_t){0u, 0u, 0u, 0u});
-      lds_write16B(do_lds + r * TL::P + c, ok ? gload16B(dO + (row0 + r) * D + c) : (u32x4_t){0u, 0u, 0u, 0u});
-    }
-    // Delta: 8 threads per row.
-    const int r = tid >> 3, part = tid & 7;
+    const srd_t rq = make_srd(q + row0 * D, (uint32_t)rows * D * 2);
+    const srd_t rdo = make_srd(dO + row0 * D, (uint32_t)rows * D * 2);
+    TL::template dma_fill<32>(rq, qd_lds, 0, wave, kWaves, lane);
+    TL::template dma_fill<32>(rdo, qd_lds + TILE, 0, wave, kWaves, lane);
+    const int r = tid >> 3, part = tid & 7;  // Delta: 8 threads per row
     float acc = 0.f;
     if (r < rows) {
       for (int d = part; d < D; d += 8) acc = fmaf(load_f32(o + (row0 + r) * D + d), to_f32<T>(dO[(row0 + r) * D + d]), acc);
@@ -385,38 +347,61 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
       dl_lds[r] = acc;
       lse_lds[r] = (r < rows) ? lse[row0 + r] * kLog2e : 0.f;
     }
+    wait_vmem();
+    __syncthreads();
   }
+  const uint8_t* qt = qd_lds;
+  const uint8_t* dt = qd_lds + TILE;
 
   const int seg = split_len / kWaves;
   const int kb0 = split * split_len + wave * seg;
   const int kb1 = min(kb0 + seg, Lkv);
-  const int steps = seg / kTileKeys;
-  uint16_t* k_lds = lds + wave * WAVE_LDS;
-  uint16_t* v_lds = k_lds + kTileKeys * TL::P;
-  uint16_t* ds_lds = v_lds + kTileKeys * TL::P;
+  const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
+  uint8_t* my = lds + wave * WAVE_LDS;
+  uint16_t* dsw = ds_lds[wave];
+  const srd_t rk = make_srd(k + kv0 * D, (uint32_t)Lkv * D * 2);
+  const srd_t rv = make_srd(v + kv0 * D, (uint32_t)Lkv * D * 2);
+  auto fill = [&](int st) {
+    uint8_t* slot = my + (st % kVecRing) * 2 * TILE;
+    TL::template dma_fill<kVecKeys, kCacheStream, false>(rk, slot, kb0 + st * kVecKeys, 0, 1, lane);
+    TL::template dma_fill<kVecKeys, kCacheStream, false>(rv, slot + TILE, kb0 + st * kVecKeys, 0, 1, lane);
+  };
+
+  // LDS geometry (as in the tiled forward): 16-byte reads of row n, chunk 2c + g; transposed
+  // reads of rows 16*c2 + 4g + L16/4 (+8), chunk 4*db + vx, byte 8*(L16&1).
+  const int G16 = lane >> 4, L16 = lane & 15;
+  const int trow = 4 * g + (L16 >> 2);
+  const int vx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
+  const int xs = g ^ TL::f(n), xt = vx ^ TL::f(trow), xt8 = vx ^ TL::f(trow + 8);
+  const int srow = n * TL::RB, trow_b = trow * TL::RB + 8 * (L16 & 1);
+  auto rd16 = [&](const uint8_t* t, int c) { return *(const u32x4_t*)(t + srow + ((2 * c) ^ xs) * 16); };
+  // A operand of 32 rows (d) x 16 k (rows 16*c2 + ... of the tile), d block db.
+  auto rdtr = [&](const uint8_t* t, int c2, int db) {
+    const uint8_t* base = t + 16 * c2 * TL::RB + trow_b;
+    const u32x2_t lo = lds_read_tr16((const uint16_t*)(base + ((4 * db) ^ xt) * 16));
+    const u32x2_t hi = lds_read_tr16((const uint16_t*)(base + 8 * TL::RB + ((4 * db) ^ xt8) * 16));
+    return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+  };
 
   f32x16_t dqa[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqa[db][i] = 0.f;
-  u32x4_t kbuf[TL::LOADS], vbuf[TL::LOADS];
-  wave_fetch<D>(kbuf, k + kv0 * D, kb0, kb1, lane);
-  wave_fetch<D>(vbuf, v + kv0 * D, kb0, kb1, lane);
-  const int G16 = lane >> 4, L16 = lane & 15;
+
+  if (steps > 0) fill(0);
   for (int st = 0; st < steps; ++st) {
-    __syncthreads();
-    wave_store<D>(k_lds, kbuf, lane);
-    wave_store<D>(v_lds, vbuf, lane);
-    __syncthreads();
-    const int t0 = kb0 + st * kTileKeys;
     if (st + 1 < steps) {
-      wave_fetch<D>(kbuf, k + kv0 * D, t0 + kTileKeys, kb1, lane);
-      wave_fetch<D>(vbuf, v + kv0 * D, t0 + kTileKeys, kb1, lane);
+      fill(st + 1);  // the slot of step st - 1: this wave's reads of it have completed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    if (t0 >= kb1) continue;
+    const uint8_t* kt = my + (st % kVecRing) * 2 * TILE;
+    const uint8_t* vt = kt + TILE;
+    const int t0 = kb0 + st * kVecKeys;
     const int key = t0 + n;  // this lane's key column
-    // S = Q K^T and dP = dO V^T: rows = query rows, columns = this wave's 32 keys.
+    // S = Q K^T and dP = dO V^T: rows = packed query rows, columns = this wave's 32 keys.
     f32x16_t s, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -425,8 +410,8 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
     }
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      s = mfma32<T>(lds_read16B(q_lds + n * TL::P + 16 * c + 8 * g), lds_read16B(k_lds + n * TL::P + 16 * c + 8 * g), s);
-      dp = mfma32<T>(lds_read16B(do_lds + n * TL::P + 16 * c + 8 * g), lds_read16B(v_lds + n * TL::P + 16 * c + 8 * g), dp);
+      s = mfma32<T>(rd16(qt, c), rd16(kt, c), s);
+      dp = mfma32<T>(rd16(dt, c), rd16(vt, c), dp);
     }
     u32x4_t pop[2], dsop[2];
 #pragma unroll
@@ -450,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
       dsop[c2] = (u32x4_t){pack2<T>(dsv[0], dsv[1]), pack2<T>(dsv[2], dsv[3]), pack2<T>(dsv[4], dsv[5]),
                            pack2<T>(dsv[6], dsv[7])};
       // dS^T scratch, row = key n, columns = query rows (4 consecutive rows per dword pair).
-      *(u32x2_t*)(ds_lds + n * TL::DSP + 16 * c2 + 4 * g) = (u32x2_t){dsop[c2][0], dsop[c2][1]};
-      *(u32x2_t*)(ds_lds + n * TL::DSP + 16 * c2 + 8 + 4 * g) = (u32x2_t){dsop[c2][2], dsop[c2][3]};
+      *(u32x2_t*)(dsw + n * DSP + 16 * c2 + 4 * g) = (u32x2_t){dsop[c2][0], dsop[c2][1]};
+      *(u32x2_t*)(dsw + n * DSP + 16 * c2 + 8 + 4 * g) = (u32x2_t){dsop[c2][2], dsop[c2][3]};
     }
     // dV^T = dO^T P and dK^T = Q^T dS for this wave's keys (complete: all rows are here).
     f32x16_t dva[D / 32], dka[D / 32];
@@ -462,14 +447,10 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
         dva[db][i] = 0.f;
         dka[db][i] = 0.f;
       }
-      const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const int row = 16 * c2 + 4 * g + (L16 >> 2);
-        const u32x2_t dlo = lds_read_tr16(do_lds + row * TL::P + col), dhi = lds_read_tr16(do_lds + (row + 8) * TL::P + col);
-        dva[db] = mfma32<T>((u32x4_t){dlo[0], dlo[1], dhi[0], dhi[1]}, pop[c2], dva[db]);
-        const u32x2_t qlo = lds_read_tr16(q_lds + row * TL::P + col), qhi = lds_read_tr16(q_lds + (row + 8) * TL::P + col);
-        dka[db] = mfma32<T>((u32x4_t){qlo[0], qlo[1], qhi[0], qhi[1]}, dsop[c2], dka[db]);
+        dva[db] = mfma32<T>(rdtr(dt, c2, db), pop[c2], dva[db]);
+        dka[db] = mfma32<T>(rdtr(qt, c2, db), dsop[c2], dka[db]);
       }
     }
     if (key < kb1) {
@@ -484,21 +465,19 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
           Store4<OutT>::run(dv + kro + d, dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2], dva[db][4 * r4 + 3]);
         }
     }
-    // dQ^T += K^T dS^T over this wave's 32 keys: chunk c2 = keys 16*c2 + 8g' .. +7.
+    wave_sync();  // the dS^T scratch written above is read across lanes below
+    // dQ^T += K^T dS^T over this wave's 32 keys; A and B use the same transposed-read rows,
+    // so their k slots pair the same keys.
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
-      const int krow = 16 * c2 + 8 * g + (L16 >> 2);
-      const u32x2_t blo = lds_read_tr16(ds_lds + krow * TL::DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
-      const u32x2_t bhi = lds_read_tr16(ds_lds + (krow + 4) * TL::DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
+      const int krow = 16 * c2 + trow;
+      const u32x2_t blo = lds_read_tr16(dsw + krow * DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
+      const u32x2_t bhi = lds_read_tr16(dsw + (krow + 8) * DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
       const u32x4_t bop = (u32x4_t){blo[0], blo[1], bhi[0], bhi[1]};
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int col = db * 32 + 16 * (G16 & 1) + 4 * (L16 & 3);
-        const u32x2_t alo = lds_read_tr16(k_lds + krow * TL::P + col);
-        const u32x2_t ahi = lds_read_tr16(k_lds + (krow + 4) * TL::P + col);
-        dqa[db] = mfma32<T>((u32x4_t){alo[0], alo[1], ahi[0], ahi[1]}, bop, dqa[db]);
-      }
+      for (int db = 0; db < D / 32; ++db) dqa[db] = mfma32<T>(rdtr(kt, c2, db), bop, dqa[db]);
     }
+    wave_sync();  // the scratch is rewritten by the next step
   }
   // Sum the 4 waves' dQ^T (lane (n, g) holds row n, d = db*32 + 8*(i/4) + 4g + i%4).
   __syncthreads();
@@ -546,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __
 template <typename T, int D, typename OutT>
 hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse, float scale,
                      void* ws, hipStream_t st) {
-  const SplitPlan pl = plan_fwd(s);
+  const SplitPlan pl = plan(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int n_rb = (int)((G * s.Lq + 31) / 32);
   const int64_t tr = rows_total(s);
@@ -592,7 +571,7 @@ hipError_t bwd_typed(const Shape& s, const void* q, const void* k, const void* v
 int vector_num_splits(const Shape& s) { return plan(s).nsplit; }
 
 size_t vector_fwd_workspace(const Shape& s) {
-  const SplitPlan pl = plan_fwd(s);
+  const SplitPlan pl = plan(s);
   if (pl.nsplit == 1) return 0;
   return (size_t)pl.nsplit * (size_t)rows_total(s) * (size_t)(s.D + 2) * sizeof(float);
 }
