@@ -453,17 +453,20 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
         dka[db] = mfma32<T>(rdtr(qt, c2, db), dsop[c2], dka[db]);
       }
     }
-    if (key < kb1) {
-      const int64_t kro = (kv0 + key) * D;
+    if constexpr (sizeof(OutT) == 4) {  // fp32 outputs: stored straight from the accumulators
+      if (key < kb1) {
+        const int64_t kro = (kv0 + key) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d = db * 32 + 8 * r4 + 4 * g;
-          Store4<OutT>::run(dk + kro + d, dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale,
-                            dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale);
-          Store4<OutT>::run(dv + kro + d, dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2], dva[db][4 * r4 + 3]);
-        }
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = db * 32 + 8 * r4 + 4 * g;
+            Store4<OutT>::run(dk + kro + d, dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale,
+                              dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale);
+            Store4<OutT>::run(dv + kro + d, dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2],
+                              dva[db][4 * r4 + 3]);
+          }
+      }
     }
     wave_sync();  // the dS^T scratch written above is read across lanes below
     // dQ^T += K^T dS^T over this wave's 32 keys; A and B use the same transposed-read rows,
@@ -477,7 +480,36 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) dqa[db] = mfma32<T>(rdtr(kt, c2, db), bop, dqa[db]);
     }
-    wave_sync();  // the scratch is rewritten by the next step
+    if constexpr (sizeof(OutT) == 2) {
+      // 16-bit outputs: stage dV and dK rows in this step's V and K slots (both consumed by
+      // now), swizzled like the input tiles, then write whole rows: 16 bytes per lane, 1 KiB
+      // per instruction, non-temporal (written once).
+      uint8_t* vs = (uint8_t*)vt;
+      uint8_t* ks = (uint8_t*)kt;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int o = TL::off(n, 4 * db + r4) + 8 * g;  // row key, d = db*32 + 8*r4 + 4g .. +3
+          *(u32x2_t*)(vs + o) = (u32x2_t){pack2<OutT>(dva[db][4 * r4], dva[db][4 * r4 + 1]),
+                                          pack2<OutT>(dva[db][4 * r4 + 2], dva[db][4 * r4 + 3])};
+          *(u32x2_t*)(ks + o) =
+              (u32x2_t){pack2<OutT>(dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale),
+                        pack2<OutT>(dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale)};
+        }
+      wave_sync();
+      constexpr int RPI = 64 / TL::CPR;  // rows per 64-lane store
+#pragma unroll
+      for (int i = 0; i < kVecKeys / RPI; ++i) {
+        const int r = i * RPI + lane / TL::CPR, c = lane % TL::CPR;
+        if (t0 + r < kb1) {
+          const int64_t go = (kv0 + t0 + r) * D + 8 * c;
+          __builtin_nontemporal_store(*(const u32x4_t*)(vs + TL::off(r, c)), (u32x4_t*)(dv + go));
+          __builtin_nontemporal_store(*(const u32x4_t*)(ks + TL::off(r, c)), (u32x4_t*)(dk + go));
+        }
+      }
+    }
+    wave_sync();  // the scratch and slots are rewritten by the next steps
   }
   // Sum the 4 waves' dQ^T (lane (n, g) holds row n, d = db*32 + 8*(i/4) + 4g + i%4).
   __syncthreads();
