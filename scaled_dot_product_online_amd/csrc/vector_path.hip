@@ -105,13 +105,19 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
   const int kb1 = min(kb0 + seg, Lkv);
   const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
 
+  // Ring of 2 K slots and 2 V slots per wave. The K slot of step st is refilled with
+  // step st + 2 as soon as S^T of step st has been read out of it, and the V slot as soon
+  // as P V has: each tile is requested about two steps before it is used.
   uint8_t* my = lds + wave * WAVE_LDS;
   const srd_t rk = make_srd(k + kv0 * D, (uint32_t)Lkv * D * 2);
   const srd_t rv = make_srd(v + kv0 * D, (uint32_t)Lkv * D * 2);
-  auto fill = [&](int st) {
-    uint8_t* slot = my + (st % kVecRing) * 2 * TILE;
-    TL::template dma_fill<kVecKeys, kCacheStream, false>(rk, slot, kb0 + st * kVecKeys, 0, 1, lane);
-    TL::template dma_fill<kVecKeys, kCacheStream, false>(rv, slot + TILE, kb0 + st * kVecKeys, 0, 1, lane);
+  auto kslot = [&](int st) { return my + (st & 1) * 2 * TILE; };
+  auto vslot = [&](int st) { return my + (st & 1) * 2 * TILE + TILE; };
+  auto fill_k = [&](int st) {
+    TL::template dma_fill<kVecKeys, kCacheStream, false>(rk, kslot(st), kb0 + st * kVecKeys, 0, 1, lane);
+  };
+  auto fill_v = [&](int st) {
+    TL::template dma_fill<kVecKeys, kCacheStream, false>(rv, vslot(st), kb0 + st * kVecKeys, 0, 1, lane);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -127,16 +133,18 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  if (steps > 0) fill(0);
+  for (int st = 0; st < 2 && st < steps; ++st) {
+    fill_k(st);
+    fill_v(st);
+  }
   for (int st = 0; st < steps; ++st) {
-    if (st + 1 < steps) {
-      fill(st + 1);  // the slot of step st - 1: this wave's reads of it have completed
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");  // step st has landed
-    } else {
+    // Loads in flight, oldest first: K(st), V(st), then K(st+1), V(st+1) if issued.
+    if (st + 1 < steps)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+    else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    const uint8_t* kt = my + (st % kVecRing) * 2 * TILE;
-    const uint8_t* vt = kt + TILE;
+    const uint8_t* kt = kslot(st);
+    const uint8_t* vt = vslot(st);
     const int t0 = kb0 + st * kVecKeys;
 
     // S^T = K Q^T: lane holds keys t0 + 8*(i/4) + 4g + i%4 of packed row n.
@@ -146,6 +154,10 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       s = mfma32<T>(*(const u32x4_t*)(kt + srow + ((2 * c) ^ xk) * 16), qop[c], s);
+    if (st + 2 < steps) {  // the K reads above have returned (S^T depends on them)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      fill_k(st + 2);
+    }
     if (t0 + kVecKeys > kb1) {  // wave-uniform: the segment ends inside this step
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -188,6 +200,10 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
         const u32x2_t hi = lds_read_tr16((const uint16_t*)(vb + 8 * TL::RB + ((4 * db) ^ xv8) * 16));
         oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop[c2], oacc[db]);
       }
+    }
+    if (st + 2 < steps) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      fill_v(st + 2);
     }
   }
   const float l = half_swap_sum(lsum);
