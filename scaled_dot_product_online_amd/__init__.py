@@ -7,6 +7,8 @@ ABI of include/sdpa.h); this package is its Python binding:
         -> (o, lse)
     sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None)
         -> (dq, dk, dv)
+    attention(q, k, v, scale=None, is_causal=False) -> o
+        differentiable (torch.autograd) wrapper over the two calls above
 
 Tensors are contiguous [B, H, L, D] torch tensors on the GPU in float32, float16
 or bfloat16; K/V may have fewer heads than Q (grouped-query attention).
@@ -28,3 +30,5 @@ from ._lib import (  # noqa: F401
     status_str,
     workspace_bytes,
 )
+
+from .autograd import attention, check_eligible  # noqa: F401,E402
