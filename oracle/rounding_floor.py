@@ -93,7 +93,7 @@ def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_b
     rows = np.asarray(rows)
     s = (qh[rows] @ kh.T) * float(scale)
     if is_causal:
-        s = np.where(np.arange(kh.shape[0])[None, :] <= rows[:, None], s, -np.inf)
+        s = np.where(np.arange(kh.shape[0])[None, :] <= rows[:, None] + (kh.shape[0] - qh.shape[0]), s, -np.inf)
     m_final = s.max(axis=1, keepdims=True)
     m_run = _running_max(s, kv_block, kv_segment, slack)
     with np.errstate(invalid="ignore"):
@@ -137,7 +137,7 @@ def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtyp
         s = (qh @ kh.T) * float(scale)
         p = np.exp(s - np.asarray(lse[b, h], dtype=np.float64)[:, None])
         if is_causal:
-            p = np.where(np.arange(Lkv)[None, :] <= np.arange(Lq)[:, None], p, 0.0)
+            p = np.where(np.arange(Lkv)[None, :] <= np.arange(Lq)[:, None] + (Lkv - Lq), p, 0.0)
         delta = np.sum(doh * np.asarray(o_stored[b, h], dtype=np.float64), axis=1)
         dp = doh @ vh.T
         ds = p * (dp - delta[:, None])

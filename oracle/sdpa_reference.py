@@ -22,8 +22,12 @@ Sources (pages, cited by title and section)
 
 Readings where the pages are silent
 -----------------------------------
-* Causal masking keeps key j for query i iff j <= i (query and key positions
-  aligned at 0; only used with Lq == Lkv).
+* Causal masking keeps key j for query i iff j <= i + (Lkv - Lq): the query and key
+  sequences are aligned at their ends (the last query sees every key, as when new
+  queries attend to a key/value cache). With Lq == Lkv this is j <= i. The pages name
+  unequal query and key lengths only as a test edge case (MLX pull request "[Metal]
+  Add Flash Attention VJP for training", "Test Plan"), not the alignment; Lq <= Lkv
+  is required so that every query row sees at least one key.
 * GQA: query head h reads key/value head h // (Hq // Hkv) (contiguous groups).
 * The logsumexp is the natural log of sum_j exp(s_ij) over the *scaled* scores.
 * The backward is the gradient of the scalar sum(O * dO) with respect to Q, K and
@@ -37,8 +41,10 @@ Readings where the pages are silent
 
 Parity pins (tests/test_oracle_pins.py): torch's CPU math attention and autograd
 in float64, scipy's logsumexp, central finite differences of sum(O * dO), the
-closed forms Lkv = 1, equal scores, causal row 0 and causal Q = 0, and the
-invariants listed there. No function in this module is "parity unpinned".
+closed forms Lkv = 1, equal scores, causal row 0 and causal Q = 0, causal with
+Lq < Lkv as the last rows of the square causal problem and with Lq = 1 as full
+attention, and the invariants listed there. No function in this module is "parity
+unpinned".
 """
 
 from __future__ import annotations
@@ -50,10 +56,13 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _causal_keep(rows, n_keys):
-    """Boolean [len(rows), n_keys]: True where key j is visible to query i (j <= i)."""
+def _causal_keep(rows, n_queries, n_keys):
+    """Boolean [len(rows), n_keys]: True where key j is visible to query i,
+    j <= i + (n_keys - n_queries) (sequences aligned at their ends)."""
+    if n_queries > n_keys:
+        raise ValueError("causal attention needs Lq <= Lkv")
     rows = np.asarray(rows)
-    return np.arange(n_keys)[None, :] <= rows[:, None]
+    return np.arange(n_keys)[None, :] <= rows[:, None] + (n_keys - n_queries)
 
 
 def head_forward(qh, kh, vh, scale, is_causal, rows=None):
@@ -68,7 +77,7 @@ def head_forward(qh, kh, vh, scale, is_causal, rows=None):
     rows = np.asarray(rows)
     s = (qh[rows] @ kh.T) * float(scale)
     if is_causal:
-        s = np.where(_causal_keep(rows, kh.shape[0]), s, -np.inf)
+        s = np.where(_causal_keep(rows, qh.shape[0], kh.shape[0]), s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)

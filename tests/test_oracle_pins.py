@@ -153,6 +153,31 @@ def test_causal_row0_and_causal_zero_q():
     assert np.abs(dk).max() < 1e-14
 
 
+def test_causal_unequal_lengths_are_the_tail_of_the_square_problem():
+    # Causal with Lq < Lkv (sequences aligned at their ends) equals the last Lq rows of
+    # the square causal problem whose queries end with the same Lq rows; the square
+    # case is pinned to torch above. Gradients: the prefix rows carry dO = 0.
+    B, Hq, Hkv, Lq, Lkv, D = 1, 4, 2, 5, 13, 8
+    qt, k, v, dot = rand(B, Hq, Lq, D), rand(B, Hkv, Lkv, D), rand(B, Hkv, Lkv, D), rand(B, Hq, Lq, D)
+    qfull = np.concatenate([rand(B, Hq, Lkv - Lq, D), qt], axis=2)
+    dofull = np.concatenate([np.zeros((B, Hq, Lkv - Lq, D)), dot], axis=2)
+    o, lse = ref.attention_forward(qt, k, v, 0.6, True)
+    of, lsef = ref.attention_forward(qfull, k, v, 0.6, True)
+    np.testing.assert_allclose(o, of[:, :, Lkv - Lq:], atol=1e-14)
+    np.testing.assert_allclose(lse, lsef[:, :, Lkv - Lq:], atol=1e-14)
+    dq, dk, dv = ref.attention_backward(qt, k, v, dot, 0.6, True)
+    dqf, dkf, dvf = ref.attention_backward(qfull, k, v, dofull, 0.6, True)
+    np.testing.assert_allclose(dq, dqf[:, :, Lkv - Lq:], atol=1e-13)
+    np.testing.assert_allclose(dk, dkf, atol=1e-13)
+    np.testing.assert_allclose(dv, dvf, atol=1e-13)
+    # One query row sees every key: causal equals full attention.
+    q1 = qt[:, :, -1:]
+    for a, b_ in zip(ref.attention_forward(q1, k, v, 0.6, True), ref.attention_forward(q1, k, v, 0.6, False)):
+        np.testing.assert_array_equal(a, b_)
+    with pytest.raises(ValueError):
+        ref.attention_forward(qfull, k[:, :, :Lq], v[:, :, :Lq], 0.6, True)
+
+
 def test_two_keys_logistic():
     q = np.array([[[[1.0, 2.0]]]])
     k = np.array([[[[0.5, -1.0], [2.0, 1.0]]]])
@@ -264,10 +289,10 @@ def test_round_to_matches_ieee_conversions():
     assert round_to(np.array([1.0 + 3 * 2.0 ** -8]), "bf16")[0] == 1.0 + 2.0 ** -6
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_rounding_model_reduces_to_definition_in_fp64(causal):
+@pytest.mark.parametrize("causal,Lq", [(False, 37), (True, 37), (True, 20)])
+def test_rounding_model_reduces_to_definition_in_fp64(causal, Lq):
     B, Hq, Hkv, L, D = 1, 4, 2, 37, 16
-    q, k, v, do = rand(B, Hq, L, D), rand(B, Hkv, L, D), rand(B, Hkv, L, D), rand(B, Hq, L, D)
+    q, k, v, do = rand(B, Hq, Lq, D), rand(B, Hkv, L, D), rand(B, Hkv, L, D), rand(B, Hq, Lq, D)
     o, lse = ref.attention_forward(q, k, v, 0.25, causal)
     oe = emulate_forward(q, k, v, 0.25, causal, "f64", "f64", kv_block=8)
     np.testing.assert_allclose(oe, o, atol=1e-13)
