@@ -22,8 +22,13 @@
  *               k, v, dk, dv : [B, Hkv, Lkv, D]
  *               lse          : [B, Hq,  Lq]   float32, natural log
  *             Query head h reads key/value head h / (Hq / Hkv).
- * Masking     is_causal != 0 keeps key j for query i iff j <= i; it requires
- *             Lq == Lkv. No other mask, no dropout.
+ * Masking     is_causal != 0 keeps key j for query i iff j <= i + (Lkv - Lq): the
+ *             query and key sequences are aligned at their ends, so the last query
+ *             sees every key (new queries against a key/value cache); with Lq == Lkv
+ *             this is j <= i. It requires Lq <= Lkv, so that every query row sees a
+ *             key. The pages list unequal query and key lengths only as a test edge
+ *             case (MLX pull request, "Test Plan"); the end alignment is this
+ *             library's reading. No other mask, no dropout.
  * Precision   dtype is the operand type of q, k, v, dO (SDPA_F32, SDPA_F16 or
  *             SDPA_BF16). Products accumulate in float32. out_dtype is the type
  *             of o, dq, dk, dv and must be dtype or SDPA_F32 (with SDPA_F32
@@ -62,7 +67,7 @@ typedef enum {
   SDPA_ERR_NULL = 1,        /* a required pointer is NULL                              */
   SDPA_ERR_SHAPE = 2,       /* a size < 1, Hq % Hkv != 0, counts overflow, or one head's
                                (L + 256) * D elements exceed 2 GiB                     */
-  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32, 64, 128}, causal with Lq != Lkv, bad dtype */
+  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32, 64, 128}, causal with Lq > Lkv, bad dtype  */
   SDPA_ERR_WORKSPACE = 4,   /* workspace smaller than sdpa_workspace_bytes()            */
   SDPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte (workspace: 256) aligned   */
   SDPA_ERR_DEVICE = 6,      /* the HIP runtime rejected a launch                        */
@@ -71,15 +76,15 @@ typedef enum {
 
 /* Kernel families, as returned by sdpa_select_path(). */
 enum {
-  SDPA_PATH_TILED = 0,  /* 16-bit operands, Lq > 8 or causal: MFMA tiles, online softmax  */
-  SDPA_PATH_VECTOR = 1, /* 16-bit, Lq <= 8, not causal, (Hq/Hkv)*Lq <= 32: keys split     */
+  SDPA_PATH_TILED = 0,  /* 16-bit operands, otherwise: MFMA tiles, online softmax         */
+  SDPA_PATH_VECTOR = 1, /* 16-bit, Lq <= 8 and (Hq/Hkv)*Lq <= 32: one pass over split keys */
   SDPA_PATH_FP32 = 2    /* float32 operands                                               */
 };
 
 /*
  * Which kernel family a call with these sizes runs (a pure host function).
  * The short-query cutoff is the MLX pull request's vector VJP condition
- * (L <= 8, "Implementation Notes"), read as the query length, non-causal, and
+ * (L <= 8, "Implementation Notes"), read as the query length (causal or not), and
  * limited to groups whose (Hq / Hkv) * Lq query rows fit one 32-row matrix block.
  * Returns one of SDPA_PATH_*, or -1 if the combination is unsupported.
  */

@@ -49,8 +49,8 @@ def check_eligible(q, k, v, is_causal=False):
         raise ValueError(f"query heads {Hq} are not a multiple of key/value heads {Hkv}")
     if D not in _HEAD_DIMS:
         raise ValueError(f"head size {D} is not supported (supported: {_HEAD_DIMS})")
-    if is_causal and Lq != k.shape[2]:
-        raise ValueError("causal attention needs equal query and key lengths")
+    if is_causal and Lq > k.shape[2]:
+        raise ValueError("causal attention needs Lq <= Lkv (sequences aligned at their ends)")
 
 
 class _Attention(torch.autograd.Function):

@@ -123,9 +123,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  const int kv_end = CAUSAL ? min(Lkv, qblk * kDqBM + kDqBM) : Lkv;
+  const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
+  const int kv_end = CAUSAL ? min(Lkv, qblk * kDqBM + kDqBM + co) : Lkv;
   const int ntiles = (kv_end + kDqBN - 1) / kDqBN;
-  const int key_lim = CAUSAL ? min(Lkv, qrow + 1) : Lkv;
+  const int key_lim = CAUSAL ? min(Lkv, qrow + 1 + co) : Lkv;
   const int G16 = lane >> 4, L16 = lane & 15;
   const int fk0 = TL::f(n);
   const int trow = 4 * g + (L16 >> 2);
@@ -235,8 +236,8 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
     const uint8_t* kt = lds + (t & 1) * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     const int kt0 = t * kDqBN;
-    if (CAUSAL && kt0 > q0 + 31) continue;
-    tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0), kt, vt, kt0);  // wave-uniform flag
+    if (CAUSAL && kt0 > q0 + 31 + co) continue;
+    tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0 + co), kt, vt, kt0);  // wave-uniform flag
   }
   if (row_ok) {
     OutT* out = dq + qoff + (int64_t)qrow * D;
@@ -313,7 +314,8 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
       dva[db][i] = 0.f;
     }
 
-  const int q_begin = CAUSAL ? (kblk * kKvBN / kKvBM) * kKvBM : 0;
+  const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
+  const int q_begin = CAUSAL ? (max(0, kblk * kKvBN - co) / kKvBM) * kKvBM : 0;
   const int ntiles = (Lq - q_begin + kKvBM - 1) / kKvBM;
   // (head, query tile) pairs, query tiles from the last one backward and the G heads of
   // each tile together: every workgroup of a KV group starts at the same (last) tile, so
@@ -423,9 +425,9 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
-            if constexpr (MASKED) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, is not before key krow
-              const int u = t0 + qm * 16 + j;  // wave-uniform part
-              p = (q4x4 < Lq - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
+            if constexpr (MASKED) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, sees key krow
+              const int u = t0 + qm * 16 + j + co;  // wave-uniform part
+              p = (q4x4 < Lq + co - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
             }
             pv[4 * h + j] = p;
             dsv[4 * h + j] = p * dp[qm][j];
@@ -469,8 +471,8 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
     const uint8_t* dt = qt + TILE;
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = tile_of(it);
-    if (CAUSAL && t0 + kKvBM - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
-    tile((t0 + kKvBM > Lq) || (CAUSAL && t0 < kw0 + 15), qt, dt, st, t0);  // wave-uniform flag
+    if (CAUSAL && t0 + kKvBM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
+    tile((t0 + kKvBM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0);  // wave-uniform flag
   }
   if (krow < Lkv) {
     const int64_t ko = kvoff + (int64_t)krow * D;

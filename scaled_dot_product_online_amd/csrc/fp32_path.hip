@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS) : Lkv;
+  const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
+  const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS + co) : Lkv;
   for (int t0 = 0; t0 < kv_end; t0 += kF32BN) {
     __syncthreads();
     TL::stage(k_lds, kh, t0, Lkv);
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     for (int j = 0; j < kF32BN; ++j) {
       float x = row_sum<R>(dot_slice<D>(qv, k_lds, j, slice)) * scale_log2;
       const int key = t0 + j;
-      if (key >= Lkv || (CAUSAL && key > qrow)) x = -INFINITY;
+      if (key >= Lkv || (CAUSAL && key > qrow + co)) x = -INFINITY;
       s[j] = x;
       tmax = fmaxf(tmax, x);
     }
@@ -138,7 +139,8 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
   }
   const float lse2 = valid ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
   const float dlt = valid ? delta[(int64_t)bh * Lq + qrow] : 0.f;
-  const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS) : Lkv;
+  const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
+  const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS + co) : Lkv;
   for (int t0 = 0; t0 < kv_end; t0 += kF32BN) {
     __syncthreads();
     TL::stage(k_lds, kh, t0, Lkv);
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
       const float dp = row_sum<R>(dot_slice<D>(dov, v_lds, j, slice));
       const int key = t0 + j;
       float p = fast_exp2(fminf(sv * scale_log2 - lse2, 0.f));
-      if (key >= Lkv || (CAUSAL && key > qrow)) p = 0.f;
+      if (key >= Lkv || (CAUSAL && key > qrow + co)) p = 0.f;
       const float ds = p * (dp - dlt);
       const float* kr = k_lds + j * TL::PITCH + slice * 33;
 #pragma unroll
@@ -191,7 +193,8 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
     dva[e] = 0.f;
   }
   // Causal: queries below the first key of this block never see it.
-  const int q_begin = CAUSAL ? (kblk * ROWS / kF32BN) * kF32BN : 0;
+  const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
+  const int q_begin = CAUSAL ? (max(0, kblk * ROWS - co) / kF32BN) * kF32BN : 0;
   for (int gi = 0; gi < G; ++gi) {
     const int hq = hk * G + gi;
     const int64_t qbase = (int64_t)(b * Hq + hq) * Lq;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
         const float sv = row_sum<R>(dot_slice<D>(kv_, q_lds, j, slice));
         const float dp = row_sum<R>(dot_slice<D>(vv, do_lds, j, slice));
         float p = fast_exp2(fminf(sv * scale_log2 - lse_lds[j], 0.f));
-        if (i >= Lq || (CAUSAL && krow > i)) p = 0.f;
+        if (i >= Lq || (CAUSAL && krow > i + co)) p = 0.f;
         const float ds = p * (dp - dl_lds[j]);
         const float* qr = q_lds + j * TL::PITCH + slice * 33;
         const float* dr = do_lds + j * TL::PITCH + slice * 33;

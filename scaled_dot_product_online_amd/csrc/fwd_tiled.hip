@@ -72,9 +72,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
   float m = -INFINITY;  // reference row max of the log2-domain scores (see kRescaleSlack)
   float lsum = 0.f;     // this lane's share of the running row sum
 
-  const int kv_end = CAUSAL ? min(Lkv, qblk * kFwdBM + kFwdBM) : Lkv;
+  // Causal: key j is visible to query i iff j <= i + co, co = Lkv - Lq >= 0 (sequences
+  // aligned at their ends; co = 0 when the lengths are equal).
+  const int co = Lkv - Lq;
+  const int kv_end = CAUSAL ? min(Lkv, qblk * kFwdBM + kFwdBM + co) : Lkv;
   const int ntiles = (kv_end + kFwdBN - 1) / kFwdBN;
-  const int key_lim = CAUSAL ? min(Lkv, qrow + 1) : Lkv;  // keys >= key_lim are masked for this row
+  const int key_lim = CAUSAL ? min(Lkv, qrow + 1 + co) : Lkv;  // keys >= key_lim are masked for this row
 
   // Per-lane LDS offsets. K rows (16-byte reads): row kb*32 + n, chunk 2c + g.
   // V^T (transposed 8-byte reads): row kb*32 + 16*c2 + 4g + L16/4 (+8), column chunk
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
     const uint8_t* kt = lds + (t & 1) * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     const int kt0 = t * kFwdBN;
-    if (CAUSAL && kt0 > q0 + 31) continue;  // tile entirely above this wave's diagonal
+    if (CAUSAL && kt0 > q0 + 31 + co) continue;  // tile entirely above this wave's diagonal
 
     // S^T = K Q^T: 32 keys x 32 queries per accumulator block.
     f32x16_t s[kFwdBN / 32];
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
       }
 
     // Mask (only tiles that reach past the diagonal or the end), then the row max on raw scores.
-    if ((kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0)) {
+    if ((kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0 + co)) {
 #pragma unroll
       for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll

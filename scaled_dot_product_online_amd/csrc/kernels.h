@@ -43,9 +43,9 @@ hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const flo
 int vector_num_splits(const Shape& s);
 size_t vector_fwd_workspace(const Shape& s);
 size_t vector_bwd_workspace(const Shape& s);
-hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v, void* o,
-                             float* lse, float scale, void* ws, hipStream_t st);
-hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v,
+hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
+                             void* o, float* lse, float scale, void* ws, hipStream_t st);
+hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
                              float scale, int stages, hipStream_t st);
 

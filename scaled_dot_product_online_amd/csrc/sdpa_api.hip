@@ -33,7 +33,7 @@ sdpa_status_t check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lkv < 1 || D < 1) return SDPA_ERR_SHAPE;
   if (Hq % Hkv != 0) return SDPA_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
-  if (is_causal && Lq != Lkv) return SDPA_ERR_UNSUPPORTED;
+  if (is_causal && Lq > Lkv) return SDPA_ERR_UNSUPPORTED;  // every query row must see a key
   if (out_dtype != dtype && out_dtype != SDPA_F32) return SDPA_ERR_UNSUPPORTED;
   if (Lq > kMaxLen || Lkv > kMaxLen) return SDPA_ERR_SHAPE;
   int64_t rq, rk, eq, ek;
@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int path_of(int64_t Hq, int64_t Hkv, int64_t Lq, int is_causal, int dtype) {
   if (dtype == SDPA_F32) return SDPA_PATH_FP32;
-  return (Lq <= 8 && !is_causal && (Hq / Hkv) * Lq <= 32) ? SDPA_PATH_VECTOR : SDPA_PATH_TILED;
+  return (Lq <= 8 && (Hq / Hkv) * Lq <= 32) ? SDPA_PATH_VECTOR : SDPA_PATH_TILED;
 }
 
 size_t delta_bytes(const Shape& s) { return align_up((size_t)(s.B * s.Hq * s.Lq) * sizeof(float)); }
@@ -106,7 +106,7 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
       return device_status(sdpa::launch_fwd_f32(s, causal, (const float*)q, (const float*)k, (const float*)v,
                                                 (float*)o, lse, scale, hs));
     case SDPA_PATH_VECTOR:
-      return device_status(sdpa::launch_fwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, q, k, v, o, lse, scale,
+      return device_status(sdpa::launch_fwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse, scale,
                                                    workspace, hs));
     default:
       return device_status(
@@ -143,7 +143,7 @@ sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, c
                                                 (const float*)o, lse, (const float*)dO, (float*)dq, (float*)dk,
                                                 (float*)dv, delta, scale, stages, hs));
     case SDPA_PATH_VECTOR:
-      return device_status(sdpa::launch_bwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, q, k, v, o, lse, dO, dq,
+      return device_status(sdpa::launch_bwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse, dO, dq,
                                                    dk, dv, workspace, scale, stages, hs));
     default:
       return device_status(sdpa::launch_bwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse,

@@ -1,4 +1,4 @@
-// Short-query attention (Lq <= 8, not causal) for 16-bit operands on gfx950.
+// Short-query attention (Lq <= 8) for 16-bit operands on gfx950.
 //
 // The MLX pull request "[Metal] Add Flash Attention VJP for training"
 // ("Implementation Notes", vector VJP for L <= 8, fp32 accumulators) treats short
@@ -63,7 +63,7 @@ SplitPlan plan(const Shape& s) {
   return SplitPlan{(int)((s.Lkv + len - 1) / len), len};
 }
 
-template <typename T, int D, typename OutT>
+template <typename T, int D, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, OutT* __restrict__ o,
@@ -99,6 +99,9 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) settle(qop[c]);
 
+  // Causal (sequences aligned at their ends): packed row r is query r % Lq of its head
+  // and sees keys up to (r % Lq) + Lkv - Lq.
+  const int qlim = CAUSAL ? (rb * 32 + n) % Lq + (Lkv - Lq) : Lkv;
   // This wave's contiguous key segment [kb0, kb1).
   const int seg = split_len / kWaves;
   const int kb0 = split * split_len + wave * seg;
@@ -158,10 +161,14 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       fill_k(st + 2);
     }
-    if (t0 + kVecKeys > kb1) {  // wave-uniform: the segment ends inside this step
+    // Wave-uniform: the segment ends inside this step, or (causal) some row's last
+    // visible key co + (row % Lq) lies inside it.
+    if (t0 + kVecKeys > kb1 || (CAUSAL && t0 + kVecKeys - 1 > Lkv - Lq)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (t0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kb1) s[i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int key = t0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= kb1 || (CAUSAL && key > qlim)) s[i] = -INFINITY;
+      }
     }
     float tmax = -INFINITY;
 #pragma unroll
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __re
 // buffer-to-LDS loads. Q and dO of the group's 32 packed rows are staged once in
 // swizzled tiles; every LDS read uses the conflict-free patterns of the tiled forward
 // (16-byte rows for the S / dP operands, transposed reads for Q^T, dO^T and K^T).
-template <typename T, int D, typename OutT>
+template <typename T, int D, bool CAUSAL, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
@@ -334,6 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
   __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kWaves][32 * DSP];
   __shared__ __attribute__((aligned(16))) float lse_lds[32];
   __shared__ __attribute__((aligned(16))) float dl_lds[32];
+  __shared__ __attribute__((aligned(16))) int lim_lds[32];  // causal: last visible key of packed row r
 
   const int split = blockIdx.x % nsplit;
   const int bhk = blockIdx.x / nsplit;
@@ -362,6 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
     if (part == 0) {
       dl_lds[r] = acc;
       lse_lds[r] = (r < rows) ? lse[row0 + r] * kLog2e : 0.f;
+      lim_lds[r] = CAUSAL ? r % Lq + (Lkv - Lq) : Lkv;
     }
     wait_vmem();
     __syncthreads();
@@ -438,11 +447,12 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
         const int r0 = 16 * c2 + 8 * h + 4 * g;
         const f32x4_t l4 = *(const f32x4_t*)(lse_lds + r0);
         const f32x4_t d4 = *(const f32x4_t*)(dl_lds + r0);
+        const i32x4_t lim4 = *(const i32x4_t*)(lim_lds + r0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 8 * c2 + 4 * h + j;
           float p = fast_exp2(fminf(s[i] * scale_log2 - l4[j], 0.f));
-          if (r0 + j >= rows || key >= kb1) p = 0.f;
+          if (r0 + j >= rows || key >= kb1 || (CAUSAL && key > lim4[j])) p = 0.f;
           pv[4 * h + j] = p;
           dsv[4 * h + j] = p * (dp[i] - d4[j]);
         }
@@ -571,8 +581,8 @@ __global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __
 }
 
 template <typename T, int D, typename OutT>
-hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse, float scale,
-                     void* ws, hipStream_t st) {
+hipError_t fwd_typed(const Shape& s, bool causal, const void* q, const void* k, const void* v, void* o, float* lse,
+                     float scale, void* ws, hipStream_t st) {
   const SplitPlan pl = plan(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int n_rb = (int)((G * s.Lq + 31) / 32);
@@ -580,9 +590,10 @@ hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v
   float* part_o = (float*)ws;
   float* part_ml = part_o + (int64_t)pl.nsplit * tr * D;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL((vec_fwd_kernel<T, D, OutT>), dim3(pl.nsplit * n_rb * s.B * s.Hkv), dim3(kThreads), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, part_o, part_ml,
-                     (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2);
+  auto kern = causal ? vec_fwd_kernel<T, D, true, OutT> : vec_fwd_kernel<T, D, false, OutT>;
+  hipLaunchKernelGGL(kern, dim3(pl.nsplit * n_rb * s.B * s.Hkv), dim3(kThreads), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, part_o, part_ml, (int)s.Hq, G, (int)s.Lq,
+                     (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   constexpr int RPB = kThreads / (D / 4);
@@ -592,15 +603,17 @@ hipError_t fwd_typed(const Shape& s, const void* q, const void* k, const void* v
 }
 
 template <typename T, int D, typename OutT>
-hipError_t bwd_typed(const Shape& s, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                     const void* dO, void* dq, void* dk, void* dv, void* ws, float scale, int stages, hipStream_t st) {
+hipError_t bwd_typed(const Shape& s, bool causal, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws, float scale, int stages,
+                     hipStream_t st) {
   const SplitPlan pl = plan(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int64_t tr = rows_total(s);
   float* dq_part = (float*)ws;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (stages & kStage0) {
-    hipLaunchKernelGGL((vec_bwd_kernel<T, D, OutT>), dim3(pl.nsplit * s.B * s.Hkv), dim3(kThreads), 0, st,
+    auto kern = causal ? vec_bwd_kernel<T, D, true, OutT> : vec_bwd_kernel<T, D, false, OutT>;
+    hipLaunchKernelGGL(kern, dim3(pl.nsplit * s.B * s.Hkv), dim3(kThreads), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
                        (const uint16_t*)dO, (OutT*)dk, (OutT*)dv, dq_part, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv,
                        pl.nsplit, (int)pl.split_len, tr, scale_log2, scale);
@@ -639,17 +652,17 @@ size_t vector_bwd_workspace(const Shape& s) {
     default: return hipErrorInvalidValue;                                                                   \
   }
 
-hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v, void* o,
-                             float* lse, float scale, void* ws, hipStream_t st) {
+hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
+                             void* o, float* lse, float scale, void* ws, hipStream_t st) {
   if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
-  SDPA_VEC_DISPATCH(fwd_typed, s, q, k, v, o, lse, scale, ws, st)
+  SDPA_VEC_DISPATCH(fwd_typed, s, causal, q, k, v, o, lse, scale, ws, st)
 }
 
-hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, const void* q, const void* k, const void* v,
+hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
                              const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
                              float scale, int stages, hipStream_t st) {
   if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
-  SDPA_VEC_DISPATCH(bwd_typed, s, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
+  SDPA_VEC_DISPATCH(bwd_typed, s, causal, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
 }
 
 }  // namespace sdpa

@@ -39,7 +39,8 @@ def test_dtype_rules(monkeypatch, dtype, match):
     [
         ((1, 6, 8, 64), (1, 4, 8, 64), False, "not a multiple"),
         ((1, 4, 8, 96), (1, 2, 8, 96), False, "head size 96"),
-        ((1, 4, 8, 64), (1, 2, 16, 64), True, "causal"),
+        ((1, 4, 16, 64), (1, 2, 8, 64), True, "causal"),
+        ((1, 4, 8, 64), (1, 2, 16, 64), True, None),  # causal, fewer queries than keys
         ((2, 4, 8, 64), (1, 2, 8, 64), False, "batch or head size"),
         ((1, 4, 8, 64), (1, 2, 8, 64), False, None),  # eligible
     ],

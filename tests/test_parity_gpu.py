@@ -22,6 +22,7 @@ CASES = [
     (1, 4, 2, 100, 100, 64, "f32", True),
     (2, 4, 1, 37, 150, 128, "f32", False),
     (1, 2, 2, 1, 1, 64, "f32", True),
+    (1, 4, 2, 37, 100, 32, "f32", True),   # causal, fewer queries than keys (ends aligned)
 ]
 for _dt in ("f16", "bf16"):
     for _d in (32, 64, 128):
@@ -34,14 +35,22 @@ for _dt in ("f16", "bf16"):
         (1, 2, 2, 256, 256, 128, _dt, True),    # MHA, exact tiles
         (1, 2, 2, 1, 1, 64, _dt, True),         # L = 1 causal (tiled path)
         (1, 2, 2, 9, 9, 64, _dt, False),        # just above the vector cutoff
-        (32, 2, 1, 8, 8, 32, _dt, True),        # large batch, causal short rows
-        # vector path (Lq <= 8, not causal)
+        (32, 2, 1, 8, 8, 32, _dt, True),        # large batch, causal short rows (vector path)
+        # causal with Lq < Lkv: sequences aligned at their ends
+        (1, 4, 2, 70, 300, 64, _dt, True),      # ragged on both axes
+        (1, 8, 2, 130, 400, 128, _dt, True),    # GQA 4:1, several tiles each way
+        (2, 2, 2, 9, 200, 32, _dt, True),       # just above the vector cutoff
+        # vector path (Lq <= 8)
         (2, 8, 2, 1, 1000, 64, _dt, False),
         (2, 8, 2, 4, 1000, 64, _dt, False),
         (2, 8, 2, 7, 333, 128, _dt, False),
         (1, 8, 1, 4, 2085, 128, _dt, False),    # 32 packed rows, ragged keys
         (3, 4, 4, 8, 1, 32, _dt, False),        # single key
         (2, 16, 4, 8, 4099, 64, _dt, False),    # several splits
+        (2, 8, 2, 8, 1000, 64, _dt, True),      # causal decode rows against a longer cache
+        (2, 8, 2, 4, 333, 128, _dt, True),
+        (1, 4, 1, 1, 200, 64, _dt, True),       # one causal query sees every key
+        (2, 16, 4, 8, 4099, 64, _dt, True),     # causal, several splits
     ]
 
 
