@@ -5,8 +5,9 @@ A step is one pass of the whole path on one batch of synthetic input: the forwar
 (O and the logsumexp) followed by the backward's two stages (dQ, then dK/dV), on
 the workload the headline metric is quoted on (bf16, GQA 8:1, causal, B=4,
 Hq=32, Hkv=4, L=4096, D=128; inputs i.i.d. N(0,1) from seed 0, resident in HBM
-before timing starts). FLOPs are counted as 4*B*Hq*Lq*Lkv*D for the forward and
-2.5x that for the backward, halved for causal masking.
+before timing starts). FLOPs are counted as 4*B*Hq*D per visible (query, key) pair
+for the forward and 2.5x that for the backward: Lq*Lkv pairs, halved for causal
+masking when Lq == Lkv (Lq*Lkv - Lq*Lq/2 when causal with fewer queries).
 
 Prints ONE JSON line (rank 0, N=1). Besides the contract fields it carries:
   roofline      the dominant kernel's algorithmic FLOPs per launch over its mean
@@ -194,8 +195,10 @@ def kernel_symbol(runner, label):
         base = {"fwd": "fwd_tiled_kernel", "bwd_stage0": "dq_kernel", "bwd_stage1": "dkv_kernel"}[label]
         return f"{base}<{t}, {c.D}, {causal}, {t}>"
     if runner.path == "vector":
-        base = {"fwd": "vec_fwd_kernel", "bwd_stage0": "vec_bwd_kernel", "bwd_stage1": "vec_dq_reduce_kernel"}[label]
-        return f"{base}<{t}, {c.D}, {t}>"
+        if label == "bwd_stage1":
+            return f"vec_dq_reduce_kernel<{c.D}, {t}>"
+        base = {"fwd": "vec_fwd_kernel", "bwd_stage0": "vec_bwd_kernel"}[label]
+        return f"{base}<{t}, {c.D}, {causal}, {t}>"
     return None
 
 

@@ -11,7 +11,11 @@ Each entry is (name, B, Hq, Hkv, Lq, Lkv, D, dtype, is_causal). Sources:
   (MLX pull request "[Metal] Add Flash Attention VJP for training", sections
   "Key Features" and "Test Plan": GQA 8:1) at a long-context training shape.
 * ``vec_*`` — the short-query path (same pull request, "Implementation Notes",
-  vector VJP for L <= 8) with Lq != Lkv ("Test Plan", edge cases).
+  vector VJP for L <= 8) with Lq != Lkv ("Test Plan", edge cases); the ``_causal``
+  one is causal decode rows against an 8192-key cache (sequences aligned at their
+  ends).
+* ``bf16_gqa8_causal_q1k_kv4k_d128`` — a causal 1024-query chunk against 4096 keys
+  (Lq != Lkv, "Test Plan"), the GQA shape above.
 """
 
 from __future__ import annotations
@@ -29,6 +33,10 @@ for _dt in ("f16", "bf16"):
     for _lq in (1, 4, 8):
         for _d in (64, 128):
             WORKLOADS.append((f"vec_{_dt}_lq{_lq}_d{_d}", 16, 32, 8, _lq, 8192, _d, _dt, False))
+WORKLOADS += [
+    ("vec_bf16_lq8_d128_causal", 16, 32, 8, 8, 8192, 128, "bf16", True),
+    ("bf16_gqa8_causal_q1k_kv4k_d128", 4, 32, 4, 1024, 4096, 128, "bf16", True),
+]
 
 BY_NAME = {w[0]: w for w in WORKLOADS}
 
@@ -37,8 +45,10 @@ HEADLINE = "bf16_gqa8_causal_4k_d128"
 
 
 def flops(B, Hq, Lq, Lkv, D, is_causal, backward=False):
-    """Counted FLOPs: 4*B*Hq*Lq*Lkv*D forward, 2.5x that for the backward, halved when causal."""
-    f = 4.0 * B * Hq * Lq * Lkv * D
-    if backward:
-        f *= 2.5
-    return f / 2 if is_causal else f
+    """Counted FLOPs: 4*B*Hq*D per (query, key) pair forward, 2.5x that for the backward.
+
+    Pairs: Lq*Lkv; causal (sequences aligned at their ends) Lq*Lkv - Lq*Lq/2, which is
+    half of Lq*Lkv when the lengths are equal (the usual "halved for causal")."""
+    pairs = Lq * Lkv - (Lq * Lq / 2.0 if is_causal else 0.0)
+    f = 4.0 * B * Hq * pairs * D
+    return f * 2.5 if backward else f
