@@ -523,6 +523,7 @@ hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, c
   switch (s.D) {
     SDPA_BWD_CASE(32)
     SDPA_BWD_CASE(64)
+    SDPA_BWD_CASE(96)
     SDPA_BWD_CASE(128)
     default:
       return hipErrorInvalidValue;

@@ -34,11 +34,13 @@ __device__ __forceinline__ void load8(const f16_t* p, float* x) { load8_16<f16_t
 template <typename OT, typename DT, int D>
 __global__ __launch_bounds__(kDeltaThreads) void delta_kernel(const OT* __restrict__ o, const DT* __restrict__ dO,
                                                               float* __restrict__ delta, int64_t rows) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  // Threads per row, 8 elements each; a power of two for the shuffle reduction (D = 96:
+  // 16 threads, the last 4 idle).
+  constexpr int TPR = (D == 96) ? 16 : D / 8;
   const int64_t row = (int64_t)blockIdx.x * (kDeltaThreads / TPR) + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && part * 8 < D) {
     float a[8], b[8];
     load8(o + row * D + part * 8, a);
     load8(dO + row * D + part * 8, b);
@@ -53,12 +55,13 @@ __global__ __launch_bounds__(kDeltaThreads) void delta_kernel(const OT* __restri
 template <typename OT, typename DT>
 hipError_t launch_od(const Shape& s, const void* o, const void* dO, float* delta, hipStream_t st) {
   const int64_t rows = s.B * s.Hq * s.Lq;
-  const int tpr = (int)(s.D / 8);
+  const int tpr = s.D == 96 ? 16 : (int)(s.D / 8);
   const int64_t rpb = kDeltaThreads / tpr;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
   switch (s.D) {
     case 32: hipLaunchKernelGGL((delta_kernel<OT, DT, 32>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
     case 64: hipLaunchKernelGGL((delta_kernel<OT, DT, 64>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
+    case 96: hipLaunchKernelGGL((delta_kernel<OT, DT, 96>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
     case 128: hipLaunchKernelGGL((delta_kernel<OT, DT, 128>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
     default: return hipErrorInvalidValue;
   }

@@ -225,11 +225,11 @@ struct SwzTile {
     if (M == 32) {
       if (CPR >= 16) return 4 * (r & 3) + ((r >> 2) & 3);      // 256-byte rows: one row per bank window
       if (CPR == 8) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);  // 128-byte rows: two rows per window
-      return (r >> 2) & 3;                                      // 64-byte rows: four rows per window
+      return (r >> 2) & 3;  // 64-byte rows: four rows per window; also 192-byte rows (D = 96)
     }
     if (CPR >= 16) return 2 * (r & 7);
     if (CPR == 8) return 2 * ((r >> 1) & 3);
-    return 2 * ((r >> 2) & 1);
+    return 2 * ((r >> 2) & 1);  // 64- and 192-byte rows
   }
   __device__ __forceinline__ static int off(int r, int c) { return r * RB + ((c ^ f(r)) << 4); }
   // LDS DMA of rows [g0, g0 + ROWS) of a range-checked row-major [rows, D] resource

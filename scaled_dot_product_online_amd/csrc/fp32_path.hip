@@ -3,8 +3,9 @@
 // The float32 workloads on the pages are small (PyTensor issue "PERF: detect
 // scaled-dot-product-attention pattern ...", "Reproducer + metrics": B=8, H=8,
 // S=128, D=64) and their stated accuracy is 1e-5 ("Acceptance criteria"), so this
-// path keeps every product and sum in fp32 and runs on the VALUs: R = D/32 lanes
-// share one row, each holding a 32-element slice. It follows the same online
+// path keeps every product and sum in fp32 and runs on the VALUs: R lanes share one
+// row, each holding a W-element slice (R = D/32 and W = 32, or R = 4 and W = 24 for
+// D = 96 so that R stays a power of two). It follows the same online
 // softmax (exp2 domain) and the same two-kernel backward without atomics as the
 // 16-bit path (MLX pull request "[Metal] Add Flash Attention VJP for training",
 // "Implementation Notes").
@@ -24,14 +25,16 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// LDS tile of kF32BN rows: slice s of a row starts at s*33 so that the R lanes
+// LDS tile of kF32BN rows: slice s of a row starts at s*(W+1) so that the R lanes
 // of a row (reading different slices of the same row) hit different banks.
 template <int D>
 struct F32Tile {
-  static constexpr int R = D / 32;
-  static constexpr int PITCH = R * 33;
+  static constexpr int R = (D == 96) ? 4 : D / 32;  // lanes per row
+  static constexpr int W = D / R;                   // elements of a lane's slice
+  static constexpr int SP = W + 1;                  // slice pitch in LDS
+  static constexpr int PITCH = R * SP;
   static constexpr int ELEMS = kF32BN * PITCH;
-  __device__ static int idx(int row, int d) { return row * PITCH + (d >> 5) * 33 + (d & 31); }
+  __device__ static int idx(int row, int d) { return row * PITCH + (d / W) * SP + d % W; }
   // Stage rows [r0, r0 + kF32BN) of a [L, D] matrix (rows >= L are zero).
   __device__ static void stage(float* lds, const float* src, int r0, int L) {
     for (int e = threadIdx.x; e < kF32BN * D; e += kF32Threads) {
@@ -43,10 +46,10 @@ struct F32Tile {
 
 template <int D>
 __device__ __forceinline__ float dot_slice(const float* x, const float* lds, int row, int slice) {
-  const float* p = lds + row * F32Tile<D>::PITCH + slice * 33;
+  const float* p = lds + row * F32Tile<D>::PITCH + slice * F32Tile<D>::SP;
   float acc = 0.f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) acc = fmaf(x[e], p[e], acc);
+  for (int e = 0; e < F32Tile<D>::W; ++e) acc = fmaf(x[e], p[e], acc);
   return acc;
 }
 
@@ -64,10 +67,10 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
   const int slice = threadIdx.x % R, qrow = qblk * ROWS + threadIdx.x / R;
   const float* kh = k + (int64_t)(b * Hkv + hk) * Lkv * D;
   const float* vh = v + (int64_t)(b * Hkv + hk) * Lkv * D;
-  float qv[32], acc[32];
+  float qv[TL::W], acc[TL::W];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    qv[e] = (qrow < Lq) ? q[((int64_t)bh * Lq + qrow) * D + slice * 32 + e] : 0.f;
+  for (int e = 0; e < TL::W; ++e) {
+    qv[e] = (qrow < Lq) ? q[((int64_t)bh * Lq + qrow) * D + slice * TL::W + e] : 0.f;
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -94,20 +97,20 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     m = m_new;
     l *= alpha;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) acc[e] *= alpha;
+    for (int e = 0; e < TL::W; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int j = 0; j < kF32BN; ++j) {
       const float p = fast_exp2(s[j] - m_use);
       l += p;
-      const float* vr = v_lds + j * TL::PITCH + slice * 33;
+      const float* vr = v_lds + j * TL::PITCH + slice * TL::SP;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc[e] = fmaf(p, vr[e], acc[e]);
+      for (int e = 0; e < TL::W; ++e) acc[e] = fmaf(p, vr[e], acc[e]);
     }
   }
   if (qrow < Lq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) o[((int64_t)bh * Lq + qrow) * D + slice * 32 + e] = acc[e] * inv;
+    for (int e = 0; e < TL::W; ++e) o[((int64_t)bh * Lq + qrow) * D + slice * TL::W + e] = acc[e] * inv;
     if (lse != nullptr && slice == 0) lse[(int64_t)bh * Lq + qrow] = (m + fast_log2(l)) * kLn2;
   }
 }
@@ -129,10 +132,10 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
   const float* kh = k + (int64_t)(b * Hkv + hk) * Lkv * D;
   const float* vh = v + (int64_t)(b * Hkv + hk) * Lkv * D;
   const bool valid = qrow < Lq;
-  const int64_t roff = ((int64_t)bh * Lq + (valid ? qrow : 0)) * D + slice * 32;
-  float qv[32], dov[32], acc[32];
+  const int64_t roff = ((int64_t)bh * Lq + (valid ? qrow : 0)) * D + slice * TL::W;
+  float qv[TL::W], dov[TL::W], acc[TL::W];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < TL::W; ++e) {
     qv[e] = valid ? q[roff + e] : 0.f;
     dov[e] = valid ? dO[roff + e] : 0.f;
     acc[e] = 0.f;
@@ -154,14 +157,14 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
       float p = fast_exp2(fminf(sv * scale_log2 - lse2, 0.f));
       if (key >= Lkv || (CAUSAL && key > qrow + co)) p = 0.f;
       const float ds = p * (dp - dlt);
-      const float* kr = k_lds + j * TL::PITCH + slice * 33;
+      const float* kr = k_lds + j * TL::PITCH + slice * TL::SP;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc[e] = fmaf(ds, kr[e], acc[e]);
+      for (int e = 0; e < TL::W; ++e) acc[e] = fmaf(ds, kr[e], acc[e]);
     }
   }
   if (valid) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) dq[roff + e] = acc[e] * scale;
+    for (int e = 0; e < TL::W; ++e) dq[roff + e] = acc[e] * scale;
   }
 }
 
@@ -183,10 +186,10 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
   const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
   const int slice = threadIdx.x % R, krow = kblk * ROWS + threadIdx.x / R;
   const bool valid = krow < Lkv;
-  const int64_t roff = ((int64_t)bhk * Lkv + (valid ? krow : 0)) * D + slice * 32;
-  float kv_[32], vv[32], dka[32], dva[32];
+  const int64_t roff = ((int64_t)bhk * Lkv + (valid ? krow : 0)) * D + slice * TL::W;
+  float kv_[TL::W], vv[TL::W], dka[TL::W], dva[TL::W];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < TL::W; ++e) {
     kv_[e] = valid ? k[roff + e] : 0.f;
     vv[e] = valid ? v[roff + e] : 0.f;
     dka[e] = 0.f;
@@ -216,10 +219,10 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
         float p = fast_exp2(fminf(sv * scale_log2 - lse_lds[j], 0.f));
         if (i >= Lq || (CAUSAL && krow > i + co)) p = 0.f;
         const float ds = p * (dp - dl_lds[j]);
-        const float* qr = q_lds + j * TL::PITCH + slice * 33;
-        const float* dr = do_lds + j * TL::PITCH + slice * 33;
+        const float* qr = q_lds + j * TL::PITCH + slice * TL::SP;
+        const float* dr = do_lds + j * TL::PITCH + slice * TL::SP;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
+        for (int e = 0; e < TL::W; ++e) {
           dva[e] = fmaf(p, dr[e], dva[e]);
           dka[e] = fmaf(ds, qr[e], dka[e]);
         }
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
   }
   if (valid) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
+    for (int e = 0; e < TL::W; ++e) {
       dk[roff + e] = dka[e] * scale;
       dv[roff + e] = dva[e];
     }
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
 template <int D, bool C>
 hipError_t fwd_typed(const Shape& s, const float* q, const float* k, const float* v, float* o, float* lse, float scale,
                      hipStream_t st) {
-  constexpr int ROWS = kF32Threads / (D / 32);
+  constexpr int ROWS = kF32Threads / F32Tile<D>::R;
   const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
   hipLaunchKernelGGL((fwd_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, o, lse,
                      (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk,
@@ -250,7 +253,7 @@ template <int D, bool C>
 hipError_t bwd_typed(const Shape& s, const float* q, const float* k, const float* v, const float* lse,
                      const float* dO, const float* delta, float* dq, float* dk, float* dv, float scale, int stages,
                      hipStream_t st) {
-  constexpr int ROWS = kF32Threads / (D / 32);
+  constexpr int ROWS = kF32Threads / F32Tile<D>::R;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (stages & kStage0) {
     const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
@@ -273,6 +276,7 @@ hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const flo
   switch (s.D) {
     case 32: return causal ? fwd_typed<32, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<32, false>(s, q, k, v, o, lse, scale, st);
     case 64: return causal ? fwd_typed<64, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<64, false>(s, q, k, v, o, lse, scale, st);
+    case 96: return causal ? fwd_typed<96, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<96, false>(s, q, k, v, o, lse, scale, st);
     case 128: return causal ? fwd_typed<128, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<128, false>(s, q, k, v, o, lse, scale, st);
     default: return hipErrorInvalidValue;
   }
@@ -288,6 +292,7 @@ hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const flo
   switch (s.D) {
     case 32: return causal ? bwd_typed<32, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<32, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     case 64: return causal ? bwd_typed<64, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<64, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 96: return causal ? bwd_typed<96, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<96, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     case 128: return causal ? bwd_typed<128, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<128, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     default: return hipErrorInvalidValue;
   }

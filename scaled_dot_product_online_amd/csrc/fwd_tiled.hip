@@ -211,6 +211,9 @@ hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, c
     case 64:
       return causal ? launch_typed<T, 64, true, OutT>(s, q, k, v, o, lse, scale, st)
                     : launch_typed<T, 64, false, OutT>(s, q, k, v, o, lse, scale, st);
+    case 96:
+      return causal ? launch_typed<T, 96, true, OutT>(s, q, k, v, o, lse, scale, st)
+                    : launch_typed<T, 96, false, OutT>(s, q, k, v, o, lse, scale, st);
     case 128:
       return causal ? launch_typed<T, 128, true, OutT>(s, q, k, v, o, lse, scale, st)
                     : launch_typed<T, 128, false, OutT>(s, q, k, v, o, lse, scale, st);

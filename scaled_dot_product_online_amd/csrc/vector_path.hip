@@ -288,8 +288,10 @@ __global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __re
                                                                const float* __restrict__ part_ml,
                                                                OutT* __restrict__ o, float* __restrict__ lse,
                                                                int64_t total_rows, int nsplit) {
-  constexpr int TPR = D / 4;  // threads per row, 4 columns each
-  const int64_t row = (int64_t)blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  constexpr int TPR = D / 4;            // threads per row, 4 columns each
+  constexpr int RPB = kThreads / TPR;  // rows per block (D = 96: 10 rows, 16 threads idle)
+  if ((int)threadIdx.x >= RPB * TPR) return;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 4;
   if (row >= total_rows) return;
   float M = -INFINITY;
@@ -524,10 +526,11 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
                         pack2<OutT>(dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale)};
         }
       wave_sync();
-      constexpr int RPI = 64 / TL::CPR;  // rows per 64-lane store
+      // 64 lanes store 64 consecutive 16-byte chunks of the [kVecKeys, D] tile per step.
+      static_assert(kVecKeys * TL::CPR % 64 == 0, "whole 64-lane store steps");
 #pragma unroll
-      for (int i = 0; i < kVecKeys / RPI; ++i) {
-        const int r = i * RPI + lane / TL::CPR, c = lane % TL::CPR;
+      for (int i = 0; i < kVecKeys * TL::CPR / 64; ++i) {
+        const int r = (64 * i + lane) / TL::CPR, c = (64 * i + lane) % TL::CPR;
         if (t0 + r < kb1) {
           const int64_t go = (kv0 + t0 + r) * D + 8 * c;
           __builtin_nontemporal_store(*(const u32x4_t*)(vs + TL::off(r, c)), (u32x4_t*)(dv + go));
@@ -647,6 +650,8 @@ size_t vector_bwd_workspace(const Shape& s) {
                                 : (out == kF32 ? FN<f16_t, 32, float>(__VA_ARGS__) : FN<f16_t, 32, f16_t>(__VA_ARGS__));   \
     case 64: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 64, float>(__VA_ARGS__) : FN<bf16_t, 64, bf16_t>(__VA_ARGS__)) \
                                 : (out == kF32 ? FN<f16_t, 64, float>(__VA_ARGS__) : FN<f16_t, 64, f16_t>(__VA_ARGS__));   \
+    case 96: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 96, float>(__VA_ARGS__) : FN<bf16_t, 96, bf16_t>(__VA_ARGS__)) \
+                                : (out == kF32 ? FN<f16_t, 96, float>(__VA_ARGS__) : FN<f16_t, 96, f16_t>(__VA_ARGS__));   \
     case 128: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 128, float>(__VA_ARGS__) : FN<bf16_t, 128, bf16_t>(__VA_ARGS__)) \
                                  : (out == kF32 ? FN<f16_t, 128, float>(__VA_ARGS__) : FN<f16_t, 128, f16_t>(__VA_ARGS__));   \
     default: return hipErrorInvalidValue;                                                                   \

@@ -44,7 +44,8 @@ def test_select_path():
     assert sd.select_path(32, 8, 9, 8192, 64, False, sd.F16) == sd.PATH_TILED
     assert sd.select_path(64, 4, 8, 8192, 64, False, sd.F16) == sd.PATH_TILED  # 16*8 rows exceed one block
     assert sd.select_path(8, 8, 128, 128, 64, False, sd.F32) == sd.PATH_FP32
-    assert sd.select_path(8, 8, 128, 128, 96, False, sd.F16) == -1           # unsupported head dim
+    assert sd.select_path(8, 8, 128, 128, 96, False, sd.F16) == sd.PATH_TILED
+    assert sd.select_path(8, 8, 128, 128, 80, False, sd.F16) == -1           # unsupported head dim
     assert sd.select_path(8, 8, 128, 64, 64, True, sd.F16) == -1             # causal needs Lq <= Lkv
     assert sd.select_path(8, 8, 64, 128, 64, True, sd.F16) == sd.PATH_TILED  # Lq < Lkv causal: ends aligned
     assert sd.select_path(8, 3, 128, 128, 64, False, sd.F16) == -1           # Hq % Hkv
@@ -84,7 +85,7 @@ def test_forward_validation_rejects_before_launch():
     assert _fwd(lib, q=0) == 1                        # NULL
     assert _fwd(lib, B=0) == 2                        # shape
     assert _fwd(lib, Hq=3, Hkv=2) == 2                # Hq % Hkv
-    assert _fwd(lib, D=96) == 3                       # head dim
+    assert _fwd(lib, D=80) == 3                       # head dim
     assert _fwd(lib, Lq=32, Lkv=16, causal=1) == 3    # causal needs Lq <= Lkv
     assert _fwd(lib, dt=1, odt=2) == 3                # out dtype must be dtype or f32
     assert _fwd(lib, dt=0, odt=1) == 3                # f32 operands need f32 outputs

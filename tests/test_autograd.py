@@ -38,7 +38,7 @@ def test_dtype_rules(monkeypatch, dtype, match):
     "shape_q,shape_k,causal,match",
     [
         ((1, 6, 8, 64), (1, 4, 8, 64), False, "not a multiple"),
-        ((1, 4, 8, 96), (1, 2, 8, 96), False, "head size 96"),
+        ((1, 4, 8, 80), (1, 2, 8, 80), False, "head size 80"),
         ((1, 4, 16, 64), (1, 2, 8, 64), True, "causal"),
         ((1, 4, 8, 64), (1, 2, 16, 64), True, None),  # causal, fewer queries than keys
         ((2, 4, 8, 64), (1, 2, 8, 64), False, "batch or head size"),

@@ -2,7 +2,7 @@
 
 Cases follow the pages' test plan (MLX pull request "[Metal] Add Flash Attention
 VJP for training", "Test Plan": vector path L = 1, 4, 7, 8; tiled L = 16 .. 256;
-head dims 32/64/128; GQA 4:1, 8:1, 16:1 and MHA; fp16/bf16/fp32; L = 1,
+head dims 32/64/96/128; GQA 4:1, 8:1, 16:1 and MHA; fp16/bf16/fp32; L = 1,
 non-power-of-two lengths, large batch, qL != kvL) at sizes the oracle finishes in
 seconds but that span several tiles and a ragged tail. Full-size workloads are in
 test_workloads_gpu.py.
@@ -23,9 +23,11 @@ CASES = [
     (2, 4, 1, 37, 150, 128, "f32", False),
     (1, 2, 2, 1, 1, 64, "f32", True),
     (1, 4, 2, 37, 100, 32, "f32", True),   # causal, fewer queries than keys (ends aligned)
+    (1, 4, 2, 70, 130, 96, "f32", True),   # head dim 96: four lanes of 24 per row
+    (1, 2, 1, 45, 45, 96, "f32", False),
 ]
 for _dt in ("f16", "bf16"):
-    for _d in (32, 64, 128):
+    for _d in (32, 64, 96, 128):
         CASES.append((1, 4, 2, 200, 200, _d, _dt, False))
         CASES.append((1, 4, 2, 200, 200, _d, _dt, True))
     CASES += [
@@ -51,6 +53,11 @@ for _dt in ("f16", "bf16"):
         (2, 8, 2, 4, 333, 128, _dt, True),
         (1, 4, 1, 1, 200, 64, _dt, True),       # one causal query sees every key
         (2, 16, 4, 8, 4099, 64, _dt, True),     # causal, several splits
+        # head dim 96 (12 16-byte chunks per row)
+        (1, 8, 2, 130, 400, 96, _dt, True),     # tiled, causal, Lq < Lkv
+        (2, 4, 1, 70, 300, 96, _dt, False),     # tiled, ragged
+        (2, 8, 2, 7, 1000, 96, _dt, False),     # vector
+        (2, 16, 4, 8, 4099, 96, _dt, True),     # vector, causal, several splits
     ]
 
 
