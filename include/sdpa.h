@@ -67,7 +67,7 @@ typedef enum {
   SDPA_ERR_NULL = 1,        /* a required pointer is NULL                              */
   SDPA_ERR_SHAPE = 2,       /* a size < 1, Hq % Hkv != 0, counts overflow, or one head's
                                (L + 256) * D elements exceed 2 GiB                     */
-  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32, 64, 96, 128}, causal with Lq > Lkv, bad dtype */
+  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32,64,96,128,256}, causal with Lq > Lkv, bad dtype */
   SDPA_ERR_WORKSPACE = 4,   /* workspace smaller than sdpa_workspace_bytes()            */
   SDPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte (workspace: 256) aligned   */
   SDPA_ERR_DEVICE = 6,      /* the HIP runtime rejected a launch                        */

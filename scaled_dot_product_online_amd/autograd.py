@@ -20,7 +20,7 @@ import torch
 from . import _lib
 
 _DTYPES = (torch.float32, torch.float16, torch.bfloat16)
-_HEAD_DIMS = (32, 64, 96, 128)
+_HEAD_DIMS = (32, 64, 96, 128, 256)
 
 
 def check_eligible(q, k, v, is_causal=False):

@@ -62,10 +62,15 @@ __device__ __forceinline__ void load_out8<f16_t>(rsrc_t r, uint32_t elem, float*
 // Stage 0: dQ, plus the per-query {LSE*log2e, Delta} pairs for stage 1
 // ---------------------------------------------------------------------------------
 constexpr int kDqBM = 128;  // query rows per workgroup
-constexpr int kDqBN = 64;   // keys per tile
+// Keys per tile: 64, or 32 at D = 256, where the resident Q/dO operands and the dQ
+// accumulators take 384 registers per lane (one wave per SIMD).
+template <int D>
+constexpr int dq_bn() {
+  return D == 256 ? 32 : 64;
+}
 
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, const OutT* __restrict__ o,
                                                          const float* __restrict__ lse,
@@ -74,6 +79,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
                                                          int Lkv, int n_qblk, int n_bh, int lq_pad,
                                                          float scale_log2, float scale) {
   using TL = SwzTile<D>;
+  constexpr int kDqBN = dq_bn<D>();
   constexpr int TILE = kDqBN * TL::RB;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];  // [buffer][K, V]
 
@@ -255,15 +261,18 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------------
 // One workgroup = 8 waves x 16 key rows = 128 keys of one (b, hk). Each wave keeps K and
 // V of its 16 keys as B operands and the dK^T, dV^T accumulators in registers (16x16x32
-// matrix-core tiles keep that state at 96 registers per lane, so two waves share a SIMD),
-// and streams Q/dO tiles of 64 queries of every query head of the group.
-constexpr int kKvWaves = 8;
-constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
-constexpr int kKvBM = 64;             // queries per tile
+// matrix-core tiles keep that state at 96 registers per lane for D = 128, so two waves
+// share a SIMD), and streams Q/dO tiles of 64 queries of every query head of the group.
+// At D = 256 that state is 192 registers, so the workgroup has 4 waves (64 keys), one
+// per SIMD, each with the whole register file.
+template <int D>
+constexpr int kv_waves() {
+  return D == 256 ? 4 : 8;
+}
+constexpr int kKvBM = 64;  // queries per tile
 
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_per_eu(kv_waves<D>() / 4, kv_waves<D>() / 4))) void dkv_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const uint16_t* __restrict__ dO,
@@ -272,6 +281,8 @@ __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2
                                                             int G, int Lq, int Lkv, int n_kblk, int n_bhk,
                                                             int lq_pad, float scale_log2, float scale) {
   using TL = SwzTile<D, 16>;
+  constexpr int kKvWaves = kv_waves<D>();
+  constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
   constexpr int TILE = kKvBM * TL::RB;
   constexpr int STAT = kKvBM * 8;       // {LSE*log2e, Delta} of the tile's queries
   constexpr int BUF = 2 * TILE + STAT;  // one buffer: Q tile, dO tile, stats
@@ -503,9 +514,10 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
     if (e != hipSuccess) return e;
   }
   if (!(stages & kStage1)) return hipSuccess;
+  constexpr int kKvBN = 16 * kv_waves<D>();
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
-  hipLaunchKernelGGL((dkv_kernel<T, D, C, OutT>), dim3(n_kblk * n_bhk), dim3(kKvThreads), 0, st, (const uint16_t*)q,
+  hipLaunchKernelGGL((dkv_kernel<T, D, C, OutT>), dim3(n_kblk * n_bhk), dim3(64 * kv_waves<D>()), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, (const f32x2_t*)rowstat,
                      (OutT*)dk, (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk, n_bhk, lq_pad, scale_log2,
                      scale);
@@ -525,6 +537,7 @@ hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, c
     SDPA_BWD_CASE(64)
     SDPA_BWD_CASE(96)
     SDPA_BWD_CASE(128)
+    SDPA_BWD_CASE(256)
     default:
       return hipErrorInvalidValue;
   }

@@ -63,6 +63,7 @@ hipError_t launch_od(const Shape& s, const void* o, const void* dO, float* delta
     case 64: hipLaunchKernelGGL((delta_kernel<OT, DT, 64>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
     case 96: hipLaunchKernelGGL((delta_kernel<OT, DT, 96>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
     case 128: hipLaunchKernelGGL((delta_kernel<OT, DT, 128>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
+    case 256: hipLaunchKernelGGL((delta_kernel<OT, DT, 256>), grid, dim3(kDeltaThreads), 0, st, (const OT*)o, (const DT*)dO, delta, rows); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -278,6 +278,7 @@ hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const flo
     case 64: return causal ? fwd_typed<64, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<64, false>(s, q, k, v, o, lse, scale, st);
     case 96: return causal ? fwd_typed<96, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<96, false>(s, q, k, v, o, lse, scale, st);
     case 128: return causal ? fwd_typed<128, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<128, false>(s, q, k, v, o, lse, scale, st);
+    case 256: return causal ? fwd_typed<256, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<256, false>(s, q, k, v, o, lse, scale, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -294,6 +295,7 @@ hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const flo
     case 64: return causal ? bwd_typed<64, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<64, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     case 96: return causal ? bwd_typed<96, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<96, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     case 128: return causal ? bwd_typed<128, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<128, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 256: return causal ? bwd_typed<256, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<256, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     default: return hipErrorInvalidValue;
   }
 }

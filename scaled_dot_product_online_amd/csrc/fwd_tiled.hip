@@ -9,7 +9,7 @@
 // request, "Implementation Notes": log2 domain, fp32 accumulators).
 //
 // Work decomposition: one workgroup = 4 waves = 128 query rows of one
-// (batch, query head); each wave owns 32 rows. Key/value tiles of 64 rows are
+// (batch, query head); each wave owns 32 rows. Key/value tiles of 64 rows (32 at D = 256) are
 // copied into LDS by direct buffer-to-LDS loads (range-checked, so rows past the
 // end arrive as zeros), double-buffered so that tile t+1 streams in while tile t
 // is consumed, and shared by the 4 waves. Tiles are stored unpadded with an XOR
@@ -28,15 +28,21 @@ namespace sdpa {
 namespace {
 
 constexpr int kFwdBM = 128;  // query rows per workgroup
-constexpr int kFwdBN = 64;   // keys per tile
 constexpr int kFwdThreads = 256;
+// Keys per tile: 64, or 32 at D = 256, where the O accumulators alone take 128 registers
+// per lane and a 64-key score block would not fit beside them.
+template <int D>
+constexpr int fwd_bn() {
+  return D == 256 ? 32 : 64;
+}
 
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
+__global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     OutT* __restrict__ o, float* __restrict__ lse, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
     float scale_log2) {
   using TL = SwzTile<D>;
+  constexpr int kFwdBN = fwd_bn<D>();
   constexpr int TILE = kFwdBN * TL::RB;  // bytes of one K or V tile
   // [buffer][K, V] tiles; buffer t & 1 holds key tile t while tile t + 1 streams into the other.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
@@ -217,6 +223,9 @@ hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, c
     case 128:
       return causal ? launch_typed<T, 128, true, OutT>(s, q, k, v, o, lse, scale, st)
                     : launch_typed<T, 128, false, OutT>(s, q, k, v, o, lse, scale, st);
+    case 256:
+      return causal ? launch_typed<T, 256, true, OutT>(s, q, k, v, o, lse, scale, st)
+                    : launch_typed<T, 256, false, OutT>(s, q, k, v, o, lse, scale, st);
     default:
       return hipErrorInvalidValue;
   }

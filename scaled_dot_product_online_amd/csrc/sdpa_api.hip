@@ -32,7 +32,7 @@ sdpa_status_t check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_
   if (!is_dtype(dtype) || !is_dtype(out_dtype)) return SDPA_ERR_UNSUPPORTED;
   if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lkv < 1 || D < 1) return SDPA_ERR_SHAPE;
   if (Hq % Hkv != 0) return SDPA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 96 && D != 128) return SDPA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 96 && D != 128 && D != 256) return SDPA_ERR_UNSUPPORTED;
   if (is_causal && Lq > Lkv) return SDPA_ERR_UNSUPPORTED;  // every query row must see a key
   if (out_dtype != dtype && out_dtype != SDPA_F32) return SDPA_ERR_UNSUPPORTED;
   if (Lq > kMaxLen || Lkv > kMaxLen) return SDPA_ERR_SHAPE;

@@ -30,12 +30,18 @@
 namespace sdpa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 256;  // combine and reduction kernels
+// Waves per workgroup of the two streaming kernels: 4, or 2 at D = 256, where a wave's
+// K/V ring (two 32-key slots of K and V) takes 64 KiB of LDS.
+template <int D>
+constexpr int vec_waves() {
+  return D == 256 ? 2 : 4;
+}
+int vec_waves_of(int64_t D) { return D == 256 ? 2 : 4; }
 
 struct SplitPlan {
   int nsplit;
-  int64_t split_len;  // keys per split, a multiple of kWaves * kVecKeys
+  int64_t split_len;  // keys per split, a multiple of (waves per workgroup) * kVecKeys
 };
 
 int64_t rows_total(const Shape& s) { return s.B * s.Hq * s.Lq; }
@@ -43,7 +49,7 @@ int64_t rows_total(const Shape& s) { return s.B * s.Hq * s.Lq; }
 // ---------------------------------------------------------------------------------
 // Forward split
 // ---------------------------------------------------------------------------------
-// One workgroup of 4 waves per CU (the plan sizes the grid to the CU count). Each wave
+// One workgroup of 4 waves (2 at D = 256) per CU (the plan sizes the grid to the CU count). Each wave
 // streams its own contiguous key segment in 32-key steps: K and V tiles go straight from
 // HBM into a two-slot LDS ring owned by the wave (direct buffer-to-LDS loads with the
 // non-temporal policy: K and V are read exactly once), so the wave only waits on its own
@@ -54,7 +60,7 @@ constexpr int kVecRing = 2;   // LDS slots per wave
 
 SplitPlan plan(const Shape& s) {
   const int64_t groups = s.B * s.Hkv * ((s.Hq / s.Hkv * s.Lq + 31) / 32);
-  const int64_t unit = kWaves * kVecKeys;  // one step per wave
+  const int64_t unit = vec_waves_of(s.D) * kVecKeys;  // one step per wave
   const int64_t units = (s.Lkv + unit - 1) / unit;
   int64_t want = (256 + groups - 1) / groups;  // about one workgroup per CU
   if (want < 1) want = 1;
@@ -64,7 +70,7 @@ SplitPlan plan(const Shape& s) {
 }
 
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, OutT* __restrict__ o,
                                                               float* __restrict__ lse, float* __restrict__ part_o,
@@ -72,6 +78,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
                                                               int Lkv, int nsplit, int split_len, int n_rb,
                                                               int64_t total_rows, float scale_log2) {
   using TL = SwzTile<D>;
+  constexpr int kWaves = vec_waves<D>();
   constexpr int TILE = kVecKeys * TL::RB;         // bytes of one K or V tile
   constexpr int WAVE_LDS = kVecRing * 2 * TILE;   // [slot][K, V]
   constexpr int NDMA = 2 * kVecKeys * TL::CPR / 64;  // buffer-to-LDS loads per step (K and V)
@@ -230,8 +237,9 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
       *(f32x4_t*)(mrg_o + (wave * 32 + n) * D + db * 32 + 8 * r4 + 4 * g) =
           (f32x4_t){oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]};
   __syncthreads();
-  // 256 threads: row = tid / 8, 8 threads per row, D/8 columns each.
-  const int mr = tid >> 3, part = tid & 7;
+  // TPM = 2 * kWaves threads per row, 4 columns at a time.
+  constexpr int TPM = 2 * kWaves;
+  const int mr = tid / TPM, part = tid % TPM;
   const int rr = rb * 32 + mr;
   float mw[kWaves], M = -INFINITY;
 #pragma unroll
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
     const int64_t grow = row0 + rr;
     if (nsplit == 1) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      for (int d = part * 4; d < D; d += 32) {
+      for (int d = part * 4; d < D; d += 4 * TPM) {
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_fwd_kernel(const uint16_t* __
       if (lse != nullptr && part == 0) lse[grow] = (M + fast_log2(L)) * kLn2;
     } else {
       float* pod = part_o + ((int64_t)split * total_rows + grow) * D;  // [split][row][D]
-      for (int d = part * 4; d < D; d += 32) {
+      for (int d = part * 4; d < D; d += 4 * TPM) {
         float x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -321,8 +329,12 @@ __global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __re
 // buffer-to-LDS loads. Q and dO of the group's 32 packed rows are staged once in
 // swizzled tiles; every LDS read uses the conflict-free patterns of the tiled forward
 // (16-byte rows for the S / dP operands, transposed reads for Q^T, dO^T and K^T).
+// At D = 256 (2 waves) the rings and the Q/dO tiles fill the whole 160 KiB of LDS, so
+// the dS^T scratch lives in the step's V tile once dP has consumed it, the per-row
+// statistics are kept in registers, and dV/dK are formed in two halves of d after the
+// dQ update, each staged as soon as it is complete.
 template <typename T, int D, bool CAUSAL, typename OutT>
-__global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               const OutT* __restrict__ o,
@@ -333,17 +345,24 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
                                                               int split_len, int64_t total_rows, float scale_log2,
                                                               float scale) {
   using TL = SwzTile<D>;
+  constexpr int kWaves = vec_waves<D>();
+  constexpr int kWgThreads = 64 * kWaves;
+  constexpr bool kTight = D == 256;              // scratch in the V tile, statistics in registers
   constexpr int TILE = kVecKeys * TL::RB;        // bytes of one 32-row tile
   constexpr int WAVE_LDS = kVecRing * 2 * TILE;  // [slot][K, V]
   constexpr int NDMA = 2 * kVecKeys * TL::CPR / 64;
   constexpr int DSP = 32 + 16;                   // dS^T scratch pitch (elements)
   static_assert(kWaves * 32 * D * 4 <= kWaves * WAVE_LDS, "dQ reduction scratch must fit in the ring LDS");
+  static_assert(!kTight || 32 * DSP * 2 <= TILE, "dS^T scratch must fit in a V tile");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kWaves * WAVE_LDS];
   __shared__ __attribute__((aligned(1024))) uint8_t qd_lds[2 * TILE];  // Q tile, dO tile
-  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kWaves][32 * DSP];
-  __shared__ __attribute__((aligned(16))) float lse_lds[32];
-  __shared__ __attribute__((aligned(16))) float dl_lds[32];
-  __shared__ __attribute__((aligned(16))) int lim_lds[32];  // causal: last visible key of packed row r
+  __shared__ __attribute__((aligned(16))) uint16_t ds_lds[kTight ? 1 : kWaves][kTight ? 8 : 32 * DSP];
+  // Per packed row r: LSE*log2e, Delta, and (causal) the last key it sees. At D = 256 these
+  // are staged in the ring before its first fill and then held in registers.
+  __shared__ __attribute__((aligned(16))) float stat_lds[kTight ? 4 : 3 * 32];
+  float* lse_lds = kTight ? (float*)lds : stat_lds;
+  float* dl_lds = lse_lds + 32;
+  int* lim_lds = (int*)(lse_lds + 64);
 
   const int split = blockIdx.x % nsplit;
   const int bhk = blockIdx.x / nsplit;
@@ -361,20 +380,33 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
     const srd_t rdo = make_srd(dO + row0 * D, (uint32_t)rows * D * 2);
     TL::template dma_fill<32>(rq, qd_lds, 0, wave, kWaves, lane);
     TL::template dma_fill<32>(rdo, qd_lds + TILE, 0, wave, kWaves, lane);
-    const int r = tid >> 3, part = tid & 7;  // Delta: 8 threads per row
+    constexpr int TPR = kWgThreads / 32;  // Delta: threads per row
+    const int r = tid / TPR, part = tid % TPR;
     float acc = 0.f;
     if (r < rows) {
-      for (int d = part; d < D; d += 8) acc = fmaf(load_f32(o + (row0 + r) * D + d), to_f32<T>(dO[(row0 + r) * D + d]), acc);
+      for (int d = part; d < D; d += TPR) acc = fmaf(load_f32(o + (row0 + r) * D + d), to_f32<T>(dO[(row0 + r) * D + d]), acc);
     }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
     if (part == 0) {
       dl_lds[r] = acc;
       lse_lds[r] = (r < rows) ? lse[row0 + r] * kLog2e : 0.f;
       lim_lds[r] = CAUSAL ? r % Lq + (Lkv - Lq) : Lkv;
     }
     wait_vmem();
+    __syncthreads();
+  }
+  // D = 256: this lane's rows 8i + 4g + j (i = 2*c2 + h below) move to registers before
+  // the ring, which holds them, is filled.
+  f32x4_t l4r[4], d4r[4];
+  i32x4_t lim4r[4];
+  if constexpr (kTight) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l4r[i] = *(const f32x4_t*)(lse_lds + 8 * i + 4 * g);
+      d4r[i] = *(const f32x4_t*)(dl_lds + 8 * i + 4 * g);
+      lim4r[i] = *(const i32x4_t*)(lim_lds + 8 * i + 4 * g);
+    }
     __syncthreads();
   }
   const uint8_t* qt = qd_lds;
@@ -385,7 +417,6 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
   const int kb1 = min(kb0 + seg, Lkv);
   const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
   uint8_t* my = lds + wave * WAVE_LDS;
-  uint16_t* dsw = ds_lds[wave];
   const srd_t rk = make_srd(k + kv0 * D, (uint32_t)Lkv * D * 2);
   const srd_t rv = make_srd(v + kv0 * D, (uint32_t)Lkv * D * 2);
   auto fill = [&](int st) {
@@ -426,6 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
     }
     const uint8_t* kt = my + (st % kVecRing) * 2 * TILE;
     const uint8_t* vt = kt + TILE;
+    uint16_t* dsw = kTight ? (uint16_t*)const_cast<uint8_t*>(vt) : ds_lds[wave];  // V is consumed once dP is formed
     const int t0 = kb0 + st * kVecKeys;
     const int key = t0 + n;  // this lane's key column
     // S = Q K^T and dP = dO V^T: rows = packed query rows, columns = this wave's 32 keys.
@@ -447,9 +479,17 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r0 = 16 * c2 + 8 * h + 4 * g;
-        const f32x4_t l4 = *(const f32x4_t*)(lse_lds + r0);
-        const f32x4_t d4 = *(const f32x4_t*)(dl_lds + r0);
-        const i32x4_t lim4 = *(const i32x4_t*)(lim_lds + r0);
+        f32x4_t l4, d4;
+        i32x4_t lim4;
+        if constexpr (kTight) {
+          l4 = l4r[2 * c2 + h];
+          d4 = d4r[2 * c2 + h];
+          lim4 = lim4r[2 * c2 + h];
+        } else {
+          l4 = *(const f32x4_t*)(lse_lds + r0);
+          d4 = *(const f32x4_t*)(dl_lds + r0);
+          lim4 = *(const i32x4_t*)(lim_lds + r0);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 8 * c2 + 4 * h + j;
@@ -466,67 +506,98 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
       *(u32x2_t*)(dsw + n * DSP + 16 * c2 + 4 * g) = (u32x2_t){dsop[c2][0], dsop[c2][1]};
       *(u32x2_t*)(dsw + n * DSP + 16 * c2 + 8 + 4 * g) = (u32x2_t){dsop[c2][2], dsop[c2][3]};
     }
-    // dV^T = dO^T P and dK^T = Q^T dS for this wave's keys (complete: all rows are here).
-    f32x16_t dva[D / 32], dka[D / 32];
+    // dV^T = dO^T P and dK^T = Q^T dS for this wave's keys (complete: all rows are here),
+    // d blocks [hh * DBH, (hh + 1) * DBH).
+    constexpr int NH = kTight ? 2 : 1, DBH = D / 32 / NH;
+    auto dkv_products = [&](int hh, f32x16_t* dva, f32x16_t* dka) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+      for (int j = 0; j < DBH; ++j) {
+        const int db = hh * DBH + j;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dva[db][i] = 0.f;
-        dka[db][i] = 0.f;
+        for (int i = 0; i < 16; ++i) {
+          dva[j][i] = 0.f;
+          dka[j][i] = 0.f;
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          dva[j] = mfma32<T>(rdtr(dt, c2, db), pop[c2], dva[j]);
+          dka[j] = mfma32<T>(rdtr(qt, c2, db), dsop[c2], dka[j]);
+        }
       }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        dva[db] = mfma32<T>(rdtr(dt, c2, db), pop[c2], dva[db]);
-        dka[db] = mfma32<T>(rdtr(qt, c2, db), dsop[c2], dka[db]);
-      }
-    }
-    if constexpr (sizeof(OutT) == 4) {  // fp32 outputs: stored straight from the accumulators
+    };
+    // fp32 outputs: stored straight from the accumulators.
+    auto store_f32 = [&](int hh, const f32x16_t* dva, const f32x16_t* dka) {
       if (key < kb1) {
         const int64_t kro = (kv0 + key) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int j = 0; j < DBH; ++j)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = db * 32 + 8 * r4 + 4 * g;
-            Store4<OutT>::run(dk + kro + d, dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale,
-                              dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale);
-            Store4<OutT>::run(dv + kro + d, dva[db][4 * r4], dva[db][4 * r4 + 1], dva[db][4 * r4 + 2],
-                              dva[db][4 * r4 + 3]);
+            const int d = (hh * DBH + j) * 32 + 8 * r4 + 4 * g;
+            Store4<OutT>::run(dk + kro + d, dka[j][4 * r4] * scale, dka[j][4 * r4 + 1] * scale,
+                              dka[j][4 * r4 + 2] * scale, dka[j][4 * r4 + 3] * scale);
+            Store4<OutT>::run(dv + kro + d, dva[j][4 * r4], dva[j][4 * r4 + 1], dva[j][4 * r4 + 2],
+                              dva[j][4 * r4 + 3]);
           }
       }
-    }
-    wave_sync();  // the dS^T scratch written above is read across lanes below
-    // dQ^T += K^T dS^T over this wave's 32 keys; A and B use the same transposed-read rows,
-    // so their k slots pair the same keys.
+    };
+    // 16-bit outputs: dV and dK rows are staged in this step's V and K slots (consumed by
+    // then), swizzled like the input tiles, and written as whole rows below.
+    uint8_t* vs = const_cast<uint8_t*>(vt);
+    uint8_t* ks = const_cast<uint8_t*>(kt);
+    auto stage16 = [&](int hh, const f32x16_t* dva, const f32x16_t* dka) {
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int krow = 16 * c2 + trow;
-      const u32x2_t blo = lds_read_tr16(dsw + krow * DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
-      const u32x2_t bhi = lds_read_tr16(dsw + (krow + 8) * DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
-      const u32x4_t bop = (u32x4_t){blo[0], blo[1], bhi[0], bhi[1]};
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) dqa[db] = mfma32<T>(rdtr(kt, c2, db), bop, dqa[db]);
-    }
-    if constexpr (sizeof(OutT) == 2) {
-      // 16-bit outputs: stage dV and dK rows in this step's V and K slots (both consumed by
-      // now), swizzled like the input tiles, then write whole rows: 16 bytes per lane, 1 KiB
-      // per instruction, non-temporal (written once).
-      uint8_t* vs = (uint8_t*)vt;
-      uint8_t* ks = (uint8_t*)kt;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int j = 0; j < DBH; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int o = TL::off(n, 4 * db + r4) + 8 * g;  // row key, d = db*32 + 8*r4 + 4g .. +3
-          *(u32x2_t*)(vs + o) = (u32x2_t){pack2<OutT>(dva[db][4 * r4], dva[db][4 * r4 + 1]),
-                                          pack2<OutT>(dva[db][4 * r4 + 2], dva[db][4 * r4 + 3])};
+          const int o = TL::off(n, 4 * (hh * DBH + j) + r4) + 8 * g;  // row key, d = db*32 + 8*r4 + 4g .. +3
+          *(u32x2_t*)(vs + o) = (u32x2_t){pack2<OutT>(dva[j][4 * r4], dva[j][4 * r4 + 1]),
+                                          pack2<OutT>(dva[j][4 * r4 + 2], dva[j][4 * r4 + 3])};
           *(u32x2_t*)(ks + o) =
-              (u32x2_t){pack2<OutT>(dka[db][4 * r4] * scale, dka[db][4 * r4 + 1] * scale),
-                        pack2<OutT>(dka[db][4 * r4 + 2] * scale, dka[db][4 * r4 + 3] * scale)};
+              (u32x2_t){pack2<OutT>(dka[j][4 * r4] * scale, dka[j][4 * r4 + 1] * scale),
+                        pack2<OutT>(dka[j][4 * r4 + 2] * scale, dka[j][4 * r4 + 3] * scale)};
         }
+    };
+    // dQ^T += K^T dS^T over this wave's 32 keys; A and B use the same transposed-read rows,
+    // so their k slots pair the same keys. Needs the dS^T scratch visible across lanes.
+    auto dq_update = [&]() {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int krow = 16 * c2 + trow;
+        const u32x2_t blo = lds_read_tr16(dsw + krow * DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
+        const u32x2_t bhi = lds_read_tr16(dsw + (krow + 8) * DSP + 16 * (G16 & 1) + 4 * (L16 & 3));
+        const u32x4_t bop = (u32x4_t){blo[0], blo[1], bhi[0], bhi[1]};
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dqa[db] = mfma32<T>(rdtr(kt, c2, db), bop, dqa[db]);
+      }
+    };
+    if constexpr (!kTight) {
+      f32x16_t dva[DBH], dka[DBH];
+      dkv_products(0, dva, dka);
+      if constexpr (sizeof(OutT) == 4) store_f32(0, dva, dka);
+      wave_sync();  // the dS^T scratch written above is read across lanes below
+      dq_update();
+      if constexpr (sizeof(OutT) == 2) stage16(0, dva, dka);
+    } else {
+      // The dS^T scratch and the staged rows share the V slot: the dQ update reads the
+      // scratch (and K) before any row is staged.
       wave_sync();
-      // 64 lanes store 64 consecutive 16-byte chunks of the [kVecKeys, D] tile per step.
+      dq_update();
+      wave_sync();  // every lane's scratch and K reads are done before the slots are overwritten
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        f32x16_t dva[DBH], dka[DBH];
+        dkv_products(hh, dva, dka);
+        if constexpr (sizeof(OutT) == 4)
+          store_f32(hh, dva, dka);
+        else
+          stage16(hh, dva, dka);
+      }
+    }
+    if constexpr (sizeof(OutT) == 2) {
+      wave_sync();
+      // 64 lanes store 64 consecutive 16-byte chunks of the [kVecKeys, D] tile per step
+      // (1 KiB per instruction, non-temporal: written once).
       static_assert(kVecKeys * TL::CPR % 64 == 0, "whole 64-lane store steps");
 #pragma unroll
       for (int i = 0; i < kVecKeys * TL::CPR / 64; ++i) {
@@ -540,7 +611,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
     }
     wave_sync();  // the scratch and slots are rewritten by the next steps
   }
-  // Sum the 4 waves' dQ^T (lane (n, g) holds row n, d = db*32 + 8*(i/4) + 4g + i%4).
+  // Sum the waves' dQ^T (lane (n, g) holds row n, d = db*32 + 8*(i/4) + 4g + i%4).
   __syncthreads();
   float* red = (float*)lds;  // kWaves * 32 * D floats
 #pragma unroll
@@ -550,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 1) void vec_bwd_kernel(const uint16_t* __
       *(f32x4_t*)(red + (wave * 32 + n) * D + db * 32 + 8 * r4 + 4 * g) =
           (f32x4_t){dqa[db][4 * r4], dqa[db][4 * r4 + 1], dqa[db][4 * r4 + 2], dqa[db][4 * r4 + 3]};
   __syncthreads();
-  for (int e = tid; e < 32 * (D / 4); e += kThreads) {
+  for (int e = tid; e < 32 * (D / 4); e += kWgThreads) {
     const int r = e / (D / 4), c = (e % (D / 4)) * 4;
     if (r >= rows) continue;
     f32x4_t a = *(const f32x4_t*)(red + r * D + c);
@@ -594,7 +665,7 @@ hipError_t fwd_typed(const Shape& s, bool causal, const void* q, const void* k, 
   float* part_ml = part_o + (int64_t)pl.nsplit * tr * D;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   auto kern = causal ? vec_fwd_kernel<T, D, true, OutT> : vec_fwd_kernel<T, D, false, OutT>;
-  hipLaunchKernelGGL(kern, dim3(pl.nsplit * n_rb * s.B * s.Hkv), dim3(kThreads), 0, st, (const uint16_t*)q,
+  hipLaunchKernelGGL(kern, dim3(pl.nsplit * n_rb * s.B * s.Hkv), dim3(64 * vec_waves<D>()), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, part_o, part_ml, (int)s.Hq, G, (int)s.Lq,
                      (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2);
   hipError_t e = hipGetLastError();
@@ -616,7 +687,7 @@ hipError_t bwd_typed(const Shape& s, bool causal, const void* q, const void* k, 
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (stages & kStage0) {
     auto kern = causal ? vec_bwd_kernel<T, D, true, OutT> : vec_bwd_kernel<T, D, false, OutT>;
-    hipLaunchKernelGGL(kern, dim3(pl.nsplit * s.B * s.Hkv), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(kern, dim3(pl.nsplit * s.B * s.Hkv), dim3(64 * vec_waves<D>()), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
                        (const uint16_t*)dO, (OutT*)dk, (OutT*)dv, dq_part, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv,
                        pl.nsplit, (int)pl.split_len, tr, scale_log2, scale);
@@ -654,6 +725,8 @@ size_t vector_bwd_workspace(const Shape& s) {
                                 : (out == kF32 ? FN<f16_t, 96, float>(__VA_ARGS__) : FN<f16_t, 96, f16_t>(__VA_ARGS__));   \
     case 128: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 128, float>(__VA_ARGS__) : FN<bf16_t, 128, bf16_t>(__VA_ARGS__)) \
                                  : (out == kF32 ? FN<f16_t, 128, float>(__VA_ARGS__) : FN<f16_t, 128, f16_t>(__VA_ARGS__));   \
+    case 256: return dt == kBF16 ? (out == kF32 ? FN<bf16_t, 256, float>(__VA_ARGS__) : FN<bf16_t, 256, bf16_t>(__VA_ARGS__)) \
+                                 : (out == kF32 ? FN<f16_t, 256, float>(__VA_ARGS__) : FN<f16_t, 256, f16_t>(__VA_ARGS__));   \
     default: return hipErrorInvalidValue;                                                                   \
   }
 

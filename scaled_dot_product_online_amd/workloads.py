@@ -16,6 +16,9 @@ Each entry is (name, B, Hq, Hkv, Lq, Lkv, D, dtype, is_causal). Sources:
   ends).
 * ``bf16_gqa8_causal_q1k_kv4k_d128`` — a causal 1024-query chunk against 4096 keys
   (Lq != Lkv, "Test Plan"), the GQA shape above.
+* ``*_d96`` and ``*_d256`` — the GQA and short-query shapes above at head dims 96
+  (listed in the same pull request's "Test Plan") and 256 (which that pull request's
+  vector VJP leaves out for lack of threadgroup memory, "Limitations").
 """
 
 from __future__ import annotations
@@ -36,6 +39,10 @@ for _dt in ("f16", "bf16"):
 WORKLOADS += [
     ("vec_bf16_lq8_d128_causal", 16, 32, 8, 8, 8192, 128, "bf16", True),
     ("bf16_gqa8_causal_q1k_kv4k_d128", 4, 32, 4, 1024, 4096, 128, "bf16", True),
+    ("bf16_gqa8_causal_4k_d96", 4, 32, 4, 4096, 4096, 96, "bf16", True),
+    ("bf16_gqa8_causal_4k_d256", 4, 32, 4, 4096, 4096, 256, "bf16", True),
+    ("vec_bf16_lq8_d96", 16, 32, 8, 8, 8192, 96, "bf16", False),
+    ("vec_bf16_lq8_d256", 16, 32, 8, 8, 8192, 256, "bf16", False),
 ]
 
 BY_NAME = {w[0]: w for w in WORKLOADS}

@@ -2,7 +2,7 @@
 
 Cases follow the pages' test plan (MLX pull request "[Metal] Add Flash Attention
 VJP for training", "Test Plan": vector path L = 1, 4, 7, 8; tiled L = 16 .. 256;
-head dims 32/64/96/128; GQA 4:1, 8:1, 16:1 and MHA; fp16/bf16/fp32; L = 1,
+head dims 32/64/96/128 and 256; GQA 4:1, 8:1, 16:1 and MHA; fp16/bf16/fp32; L = 1,
 non-power-of-two lengths, large batch, qL != kvL) at sizes the oracle finishes in
 seconds but that span several tiles and a ragged tail. Full-size workloads are in
 test_workloads_gpu.py.
@@ -25,6 +25,7 @@ CASES = [
     (1, 4, 2, 37, 100, 32, "f32", True),   # causal, fewer queries than keys (ends aligned)
     (1, 4, 2, 70, 130, 96, "f32", True),   # head dim 96: four lanes of 24 per row
     (1, 2, 1, 45, 45, 96, "f32", False),
+    (1, 4, 1, 50, 90, 256, "f32", True),   # head dim 256: eight lanes of 32 per row
 ]
 for _dt in ("f16", "bf16"):
     for _d in (32, 64, 96, 128):
@@ -58,6 +59,13 @@ for _dt in ("f16", "bf16"):
         (2, 4, 1, 70, 300, 96, _dt, False),     # tiled, ragged
         (2, 8, 2, 7, 1000, 96, _dt, False),     # vector
         (2, 16, 4, 8, 4099, 96, _dt, True),     # vector, causal, several splits
+        # head dim 256 (32-key forward / dQ tiles, 4-wave dK/dV, 2-wave short-query kernels)
+        (1, 4, 2, 200, 200, 256, _dt, True),    # tiled, causal
+        (1, 4, 1, 70, 300, 256, _dt, False),    # tiled, ragged
+        (1, 8, 2, 130, 400, 256, _dt, True),    # tiled, causal, Lq < Lkv
+        (2, 8, 2, 7, 1000, 256, _dt, False),    # vector
+        (1, 8, 1, 4, 2085, 256, _dt, True),     # vector, causal, 32 packed rows
+        (2, 16, 4, 8, 4099, 256, _dt, False),   # vector, several splits
     ]
 
 
