@@ -23,6 +23,8 @@ Forward, with the scores kept exact:
   keys, when the block's maximum exceeds it by more than ``slack``; the
   unrounded exponentials form the denominator;
 * the output is rounded to the output dtype.
+A mask enters the scores as in the definition; a sink starts every row's reference
+maximum (the kernels enter it before the first key block) and joins the denominator.
 Backward:
 * Delta_i uses the *stored* (rounded) forward output, as the kernel does;
 * P (from the exact logsumexp) is rounded before the dV product, dS before the dQ
@@ -61,12 +63,12 @@ def round_to(x, dtype):
     raise ValueError(f"unknown dtype {dtype!r}; expected one of {_DTYPES}")
 
 
-def _running_max(s, kv_block, kv_segment, slack=0.0):
+def _running_max(s, kv_block, kv_segment, slack=0.0, start=-np.inf):
     """Per score element, the row's reference maximum in force when its key block is processed.
 
-    The reference starts at -inf at every segment start and is replaced by a block's
-    maximum when that maximum exceeds it by more than ``slack`` (natural-log units);
-    with slack 0 this is the ordinary running maximum."""
+    The reference starts at ``start`` (-inf, or the sink) at every segment start and is
+    replaced by a block's maximum when that maximum exceeds it by more than ``slack``
+    (natural-log units); with slack 0 this is the ordinary running maximum."""
     n, L = s.shape
     nblk = -(-L // kv_block)
     pad = np.full((n, nblk * kv_block), -np.inf)
@@ -77,15 +79,24 @@ def _running_max(s, kv_block, kv_segment, slack=0.0):
         raise ValueError("kv_segment must be a multiple of kv_block")
     run = np.empty_like(bmax)
     for s0 in range(0, nblk, seg_blocks):
-        m = np.full(n, -np.inf)
+        m = np.full(n, float(start))
         for j in range(s0, min(s0 + seg_blocks, nblk)):
             m = np.where(bmax[:, j] > m + slack, bmax[:, j], m)
             run[:, j] = m
     return np.repeat(run, kv_block, axis=1)[:, :L]
 
 
+def _bias_of(mask, B, Hq, Lq, Lkv, b, h):
+    """[Lq, Lkv] additive bias of (b, h): 0 / -inf for a boolean mask, the values of a float one."""
+    if mask is None:
+        return None
+    m = np.asarray(mask)
+    full = np.where(m, 0.0, -np.inf) if m.dtype == np.bool_ else m.astype(np.float64)
+    return np.broadcast_to(full, (B, Hq, Lq, Lkv))[b, h]
+
+
 def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None, rows=None,
-                         slack=0.0):
+                         slack=0.0, bias=None, sink=None):
     """Modelled kernel output O (already rounded to ``out_dtype``) for one head."""
     qh, kh, vh = (np.asarray(a, dtype=np.float64) for a in (qh, kh, vh))
     if rows is None:
@@ -94,35 +105,45 @@ def emulate_forward_head(qh, kh, vh, scale, is_causal, op_dtype, out_dtype, kv_b
     s = (qh[rows] @ kh.T) * float(scale)
     if is_causal:
         s = np.where(np.arange(kh.shape[0])[None, :] <= rows[:, None] + (kh.shape[0] - qh.shape[0]), s, -np.inf)
-    m_final = s.max(axis=1, keepdims=True)
-    m_run = _running_max(s, kv_block, kv_segment, slack)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)[rows]
+    start = -np.inf if sink is None else float(sink)
+    m_final = np.maximum(s.max(axis=1, keepdims=True), start)
+    m_final = np.where(np.isfinite(m_final), m_final, 0.0)
+    m_run = _running_max(s, kv_block, kv_segment, slack, start)
     with np.errstate(invalid="ignore"):
         p_tilde = np.where(np.isfinite(s), np.exp(s - m_run), 0.0)
         w = np.where(np.isfinite(m_run), np.exp(m_run - m_final), 0.0)
     r = round_to(p_tilde, op_dtype) * w
-    denom = np.exp(s - m_final).sum(axis=1, keepdims=True)
-    return round_to((r @ vh) / denom, out_dtype)
+    denom = np.exp(s - m_final).sum(axis=1, keepdims=True) + np.exp(start - m_final)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where(denom > 0, (r @ vh) / denom, 0.0)
+    return round_to(out, out_dtype)
 
 
-def emulate_forward(q, k, v, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None, slack=0.0):
+def emulate_forward(q, k, v, scale, is_causal, op_dtype, out_dtype, kv_block, kv_segment=None, slack=0.0, mask=None,
+                    sinks=None):
     """Modelled kernel output O [B,Hq,Lq,D], rounded to ``out_dtype``."""
-    B, Hq = q.shape[:2]
+    B, Hq, Lq = q.shape[:3]
+    Lkv = k.shape[2]
     G = Hq // k.shape[1]
     o = np.empty(q.shape, dtype=np.float64)
     for b in range(B):
         for h in range(Hq):
             o[b, h] = emulate_forward_head(q[b, h], k[b, h // G], v[b, h // G], scale, is_causal,
-                                           op_dtype, out_dtype, kv_block, kv_segment, slack=slack)
+                                           op_dtype, out_dtype, kv_block, kv_segment, slack=slack,
+                                           bias=_bias_of(mask, B, Hq, Lq, Lkv, b, h),
+                                           sink=None if sinks is None else sinks[h])
     return o
 
 
-def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, b, hk):
+def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, b, hk, mask=None):
     """Modelled dQ [G,Lq,D], dK, dV [Lkv,D] of KV group (b, hk), rounded to ``out_dtype``.
 
     ``o_stored`` and ``lse`` are the forward's stored output and logsumexp
-    ([B,Hq,Lq,D] and [B,Hq,Lq]).
+    ([B,Hq,Lq,D] and [B,Hq,Lq]); a sink acts only through the logsumexp.
     """
-    Hq, Hkv = q.shape[1], k.shape[1]
+    B, Hq, Hkv = q.shape[0], q.shape[1], k.shape[1]
     G = Hq // Hkv
     kh = np.asarray(k[b, hk], dtype=np.float64)
     vh = np.asarray(v[b, hk], dtype=np.float64)
@@ -135,7 +156,12 @@ def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtyp
         qh = np.asarray(q[b, h], dtype=np.float64)
         doh = np.asarray(do[b, h], dtype=np.float64)
         s = (qh @ kh.T) * float(scale)
-        p = np.exp(s - np.asarray(lse[b, h], dtype=np.float64)[:, None])
+        bias = _bias_of(mask, B, Hq, Lq, Lkv, b, h)
+        if bias is not None:
+            s = s + bias
+        lse_h = np.asarray(lse[b, h], dtype=np.float64)[:, None]
+        with np.errstate(invalid="ignore"):
+            p = np.where(np.isfinite(lse_h), np.exp(s - lse_h), 0.0)
         if is_causal:
             p = np.where(np.arange(Lkv)[None, :] <= np.arange(Lq)[:, None] + (Lkv - Lq), p, 0.0)
         delta = np.sum(doh * np.asarray(o_stored[b, h], dtype=np.float64), axis=1)
@@ -149,7 +175,7 @@ def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtyp
     return round_to(dq, out_dtype), round_to(dk, out_dtype), round_to(dv, out_dtype)
 
 
-def emulate_backward(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype):
+def emulate_backward(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, mask=None):
     """Modelled dQ, dK, dV for all groups, rounded to ``out_dtype``."""
     B, Hq = q.shape[:2]
     Hkv = k.shape[1]
@@ -160,5 +186,5 @@ def emulate_backward(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out
     for b in range(B):
         for hk in range(Hkv):
             dq[b, hk * G:(hk + 1) * G], dk[b, hk], dv[b, hk] = emulate_backward_group(
-                q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, b, hk)
+                q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, b, hk, mask=mask)
     return dq, dk, dv
