@@ -28,7 +28,8 @@
  *             this is j <= i. It requires Lq <= Lkv, so that every query row sees a
  *             key. The pages list unequal query and key lengths only as a test edge
  *             case (MLX pull request, "Test Plan"); the end alignment is this
- *             library's reading. No other mask, no dropout.
+ *             library's reading. Boolean and additive masks and attention sinks
+ *             are taken by sdpa_fwd_masked / sdpa_bwd_masked below. No dropout.
  * Precision   dtype is the operand type of q, k, v, dO (SDPA_F32, SDPA_F16 or
  *             SDPA_BF16). Products accumulate in float32. out_dtype is the type
  *             of o, dq, dk, dv and must be dtype or SDPA_F32 (with SDPA_F32
@@ -67,11 +68,12 @@ typedef enum {
   SDPA_ERR_NULL = 1,        /* a required pointer is NULL                              */
   SDPA_ERR_SHAPE = 2,       /* a size < 1, Hq % Hkv != 0, counts overflow, or one head's
                                (L + 256) * D elements exceed 2 GiB                     */
-  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32,64,96,128,256}, causal with Lq > Lkv, bad dtype */
+  SDPA_ERR_UNSUPPORTED = 3, /* D not in {32,64,96,128,256}, causal with Lq > Lkv or with a
+                               mask, bad dtype                                          */
   SDPA_ERR_WORKSPACE = 4,   /* workspace smaller than sdpa_workspace_bytes()            */
   SDPA_ERR_ALIGN = 5,       /* a base pointer is not 16-byte (workspace: 256) aligned   */
   SDPA_ERR_DEVICE = 6,      /* the HIP runtime rejected a launch                        */
-  SDPA_ERR_VALUE = 7        /* scale is not finite, or an invalid stage number          */
+  SDPA_ERR_VALUE = 7        /* scale not finite, invalid stage number or mask kind      */
 } sdpa_status_t;
 
 /* Kernel families, as returned by sdpa_select_path(). */
@@ -145,6 +147,66 @@ sdpa_status_t sdpa_bwd_stage(int stage, const void* q, const void* k, const void
                              const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
                              int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype,
                              sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention masks and sinks
+ * -------------------------
+ * The pages name float masks, boolean masks with False entries and attention sinks
+ * only as cases that fused paths hand back to unfused attention (mps-flash-sdpa
+ * 0.1.0, "When MFA Dispatches vs. Falls Back"; MLX pull request, "Limitations"), and
+ * place a mask as a term added to the scaled scores before the softmax (PyTensor
+ * issue, "Important guards in the matcher"). This library reads them as PyTorch's
+ * scaled_dot_product_attention does:
+ *
+ *   s_ij  = scale * q_i . k_j + bias_ij       (bias_ij = 0 / -inf for a boolean mask)
+ *   LSE_i = log(exp(sink_h) + sum_j exp(s_ij))  (no sink term when sinks is NULL)
+ *   o_i   = sum_j exp(s_ij - LSE_i) v_j
+ *
+ *   mask_kind   SDPA_MASK_NONE: no mask (mask and its strides are ignored);
+ *               SDPA_MASK_BOOL: uint8 elements, nonzero = the key takes part;
+ *               SDPA_MASK_ADDITIVE: elements of `dtype` added to the scaled scores
+ *               (finite or -inf; +inf and NaN are not allowed and not checked).
+ *   mask        device memory; element (b, h, i, j) of query head h is
+ *                 mask[b * mask_stride_b + h * mask_stride_h + i * mask_stride_q + j]
+ *               (strides in elements, >= 0; 0 broadcasts that dimension; keys are
+ *               contiguous). Additive masks are aligned to their element size.
+ *   sinks       NULL, or float32 [Hq] on the device: one logit per query head in the
+ *               units of the scaled scores; -inf means no sink for that head.
+ *
+ * A mask cannot be combined with is_causal != 0 (SDPA_ERR_UNSUPPORTED). A row that
+ * sees no key and has no sink gets o = 0 and lse = -inf, and contributes no gradient.
+ * The mask is a constant: no gradient is formed for it.
+ */
+typedef enum { SDPA_MASK_NONE = 0, SDPA_MASK_BOOL = 1, SDPA_MASK_ADDITIVE = 2 } sdpa_mask_kind_t;
+
+/*
+ * sdpa_fwd with a mask and/or sinks (definitions above). Other arguments, the
+ * workspace (sdpa_workspace_bytes with the same sizes) and errors as for sdpa_fwd;
+ * additionally SDPA_ERR_VALUE for an unknown mask_kind, SDPA_ERR_NULL for a missing
+ * mask, SDPA_ERR_SHAPE for a negative stride or an element offset that overflows, and
+ * SDPA_ERR_ALIGN for a misaligned additive mask.
+ */
+sdpa_status_t sdpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                              int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal,
+                              sdpa_mask_kind_t mask_kind, const void* mask, int64_t mask_stride_b,
+                              int64_t mask_stride_h, int64_t mask_stride_q, const float* sinks, sdpa_dtype_t dtype,
+                              sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_bwd with a mask and/or sinks: `o` and `lse` must be what sdpa_fwd_masked wrote
+ * with the same mask and sinks. With sinks != NULL, dsinks (float32 [Hq], device,
+ * required then) receives the gradient of sum(O * dO) with respect to the sinks,
+ *   dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * sum_d dO[b,h,i,d] o[b,h,i,d],
+ * summed in a fixed order (deterministic). Other arguments and errors as for sdpa_bwd
+ * and sdpa_fwd_masked.
+ */
+sdpa_status_t sdpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal,
+                              sdpa_mask_kind_t mask_kind, const void* mask, int64_t mask_stride_b,
+                              int64_t mask_stride_h, int64_t mask_stride_q, const float* sinks, float* dsinks,
+                              sdpa_dtype_t dtype, sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Static string naming a status code. Never NULL. */
 const char* sdpa_status_str(sdpa_status_t status);

@@ -188,3 +188,16 @@ def emulate_backward(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out
             dq[b, hk * G:(hk + 1) * G], dk[b, hk], dv[b, hk] = emulate_backward_group(
                 q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, b, hk, mask=mask)
     return dq, dk, dv
+
+
+def emulate_sink_gradient(do, o_stored, lse, sinks):
+    """Modelled dsinks [Hq]: the kernel forms Delta from the *stored* output, then
+    -sum_{b,i} exp(sink_h - LSE_i) Delta_i exactly (float64 here); returns
+    (dsinks, magnitude) where magnitude[h] = sum_{b,i} |exp(sink_h - LSE_i) Delta_i|,
+    the scale of the sum's rounding error."""
+    do = np.asarray(do, dtype=np.float64)
+    delta = np.sum(do * np.asarray(o_stored, dtype=np.float64), axis=3)
+    s = np.asarray(sinks, dtype=np.float64)[None, :, None]
+    with np.errstate(invalid="ignore"):
+        w = np.where(np.isfinite(s), np.exp(s - np.asarray(lse, dtype=np.float64)), 0.0)
+    return -np.sum(w * delta, axis=(0, 2)), np.sum(np.abs(w * delta), axis=(0, 2))

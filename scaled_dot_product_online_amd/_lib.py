@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_PKG_DIR, "libsdpa_mi355x.so")
 F32, F16, BF16 = 0, 1, 2
 PATH_TILED, PATH_VECTOR, PATH_FP32 = 0, 1, 2
 PATH_NAMES = {PATH_TILED: "tiled", PATH_VECTOR: "vector", PATH_FP32: "fp32"}
-SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_stage", "sdpa_status_str")
+MASK_NONE, MASK_BOOL, MASK_ADDITIVE = 0, 1, 2
+SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_stage", "sdpa_fwd_masked",
+           "sdpa_bwd_masked", "sdpa_status_str")
 
 _lib = None
 
@@ -50,6 +52,11 @@ def library():
     lib.sdpa_bwd.restype = c_int
     lib.sdpa_bwd_stage.argtypes = [c_int] + lib.sdpa_bwd.argtypes
     lib.sdpa_bwd_stage.restype = c_int
+    mask_args = [c_int, vp, i64, i64, i64]
+    lib.sdpa_fwd_masked.argtypes = lib.sdpa_fwd.argtypes[:13] + mask_args + [vp] + lib.sdpa_fwd.argtypes[13:]
+    lib.sdpa_fwd_masked.restype = c_int
+    lib.sdpa_bwd_masked.argtypes = lib.sdpa_bwd.argtypes[:17] + mask_args + [vp, vp] + lib.sdpa_bwd.argtypes[17:]
+    lib.sdpa_bwd_masked.restype = c_int
     lib.sdpa_status_str.argtypes = [c_int]
     lib.sdpa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -111,9 +118,53 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous [B, H, L, D]")
 
 
+def mask_args(attn_mask, B, Hq, Lq, Lkv, dtype_code):
+    """(kind, tensor, stride_b, stride_h, stride_q) for a torch mask broadcastable to [B,Hq,Lq,Lkv].
+
+    A boolean mask keeps the keys where it is True; any other mask must have the
+    operand dtype and is added to the scaled scores. Broadcast dimensions are passed
+    as stride 0 (no copy); only a mask whose key dimension is broadcast or strided is
+    copied, along that dimension."""
+    import torch
+
+    if attn_mask is None:
+        return MASK_NONE, None, 0, 0, 0
+    m = attn_mask
+    if m.device.type != "cuda":
+        raise ValueError("attn_mask must be on the GPU")
+    if m.dtype == torch.bool:
+        kind = MASK_BOOL
+    elif m.dtype == _torch_dtype(dtype_code):
+        kind = MASK_ADDITIVE
+    else:
+        raise TypeError(f"attn_mask must be bool or {_torch_dtype(dtype_code)}, got {m.dtype}")
+    if m.dim() > 4:
+        raise ValueError(f"attn_mask has {m.dim()} dimensions; at most 4 ([B, Hq, Lq, Lkv])")
+    m = m.reshape((1,) * (4 - m.dim()) + tuple(m.shape))
+    if m.shape[3] != Lkv or m.stride(3) != 1:
+        m = m.expand(m.shape[0], m.shape[1], m.shape[2], Lkv).contiguous()
+    e = m.expand(B, Hq, Lq, Lkv)  # raises if not broadcastable
+    return kind, m, e.stride(0), e.stride(1), e.stride(2)
+
+
+def _sinks_arg(sinks, Hq):
+    import torch
+
+    if sinks is None:
+        return None
+    if sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,) or not sinks.is_contiguous():
+        raise ValueError(f"sinks must be a contiguous float32 tensor of shape ({Hq},)")
+    if sinks.device.type != "cuda":
+        raise ValueError("sinks must be on the GPU")
+    return sinks
+
+
 def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True, out=None, lse=None,
-             workspace=None, stream=None):
-    """O (and LSE when ``need_lse``) for BHLD tensors q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D]."""
+             workspace=None, stream=None, attn_mask=None, sinks=None):
+    """O (and LSE when ``need_lse``) for BHLD tensors q [B,Hq,Lq,D], k/v [B,Hkv,Lkv,D].
+
+    ``attn_mask`` (bool, or the operand dtype: added to the scaled scores) broadcasts to
+    [B,Hq,Lq,Lkv]; ``sinks`` is a float32 [Hq] tensor of per-head sink logits."""
     import torch
 
     _contig(q, k, v)
@@ -132,19 +183,25 @@ def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True
     nws = workspace_bytes(0, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
-    st = library().sdpa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lkv, D, scale,
-                            int(bool(is_causal)), dt, odt, _ptr(workspace),
-                            workspace.numel() if workspace is not None else 0, _stream(q.device, stream))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)))
+    tail = (dt, odt, _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(q.device, stream))
+    if attn_mask is None and sinks is None:
+        st = library().sdpa_fwd(*head, *tail)
+    else:
+        kind, m, sb, sh, sq = mask_args(attn_mask, B, Hq, Lq, Lkv, dt)
+        st = library().sdpa_fwd_masked(*head, kind, _ptr(m), sb, sh, sq, _ptr(_sinks_arg(sinks, Hq)), *tail)
     _check(st)
     return out, lse
 
 
 def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, stage=None):
+             workspace=None, stream=None, stage=None, attn_mask=None, sinks=None):
     """dQ, dK, dV of sum(O * dO); ``o`` and ``lse`` are what sdpa_fwd returned.
 
     ``stage`` None runs the whole backward; 0 or 1 runs one stage (sdpa_bwd_stage),
-    in which case the same ``workspace`` must be passed to both stages."""
+    in which case the same ``workspace`` must be passed to both stages. With
+    ``attn_mask`` or ``sinks`` (as given to sdpa_fwd) the whole backward runs through
+    sdpa_bwd_masked; with ``sinks`` the result is (dq, dk, dv, dsinks)."""
     import torch
 
     _contig(q, k, v, o, lse, dO)
@@ -161,9 +218,18 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
     nws = workspace_bytes(1, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
     if workspace is None:
         workspace = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
-            B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)), dt, odt, _ptr(workspace), workspace.numel(),
-            _stream(q.device, stream))
-    st = library().sdpa_bwd(*args) if stage is None else library().sdpa_bwd_stage(int(stage), *args)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)))
+    tail = (dt, odt, _ptr(workspace), workspace.numel(), _stream(q.device, stream))
+    if attn_mask is None and sinks is None:
+        st = library().sdpa_bwd(*head, *tail) if stage is None else library().sdpa_bwd_stage(int(stage), *head, *tail)
+        _check(st)
+        return dq, dk, dv
+    if stage is not None:
+        raise ValueError("the masked backward runs as one call (no stage argument)")
+    kind, m, sb, sh, sq = mask_args(attn_mask, B, Hq, Lq, Lkv, dt)
+    sk = _sinks_arg(sinks, Hq)
+    dsinks = torch.empty(Hq, dtype=torch.float32, device=q.device) if sk is not None else None
+    st = library().sdpa_bwd_masked(*head, kind, _ptr(m), sb, sh, sq, _ptr(sk), _ptr(dsinks), *tail)
     _check(st)
-    return dq, dk, dv
+    return (dq, dk, dv) if sk is None else (dq, dk, dv, dsinks)

@@ -69,7 +69,7 @@ constexpr int dq_bn() {
   return D == 256 ? 32 : 64;
 }
 
-template <typename T, int D, bool CAUSAL, typename OutT>
+template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
 __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, const OutT* __restrict__ o,
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
                                                          const uint16_t* __restrict__ dO, OutT* __restrict__ dq,
                                                          f32x2_t* __restrict__ rowstat, int Hq, int G, int Lq,
                                                          int Lkv, int n_qblk, int n_bh, int lq_pad,
-                                                         float scale_log2, float scale) {
+                                                         float scale_log2, float scale, Mask mask) {
   using TL = SwzTile<D>;
   constexpr int kDqBN = dq_bn<D>();
   constexpr int TILE = kDqBN * TL::RB;
@@ -120,7 +120,11 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) settle(qop[c]);
   const bool row_ok = qrow < Lq;
-  const float lse2 = row_ok ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
+  float lse2 = row_ok ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
+  // A masked row that sees no key (LSE = -inf) has P = 0: +inf makes every exponent -inf.
+  if (HAS_MASK && lse2 == -INFINITY) lse2 = INFINITY;
+  const int64_t mrow =
+      HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
   if (row_ok && g == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, dlt};
 
   f32x16_t acc[D / 32];
@@ -191,16 +195,21 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
       // dS^T as B operands, one per 16-key half c2. Only the softmax is duplicated for
       // the masked case (a wave-uniform branch), so both paths share the same registers.
       u32x4_t dsop[2];
-      auto softmax = [&](auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
+      auto softmax = [&](auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           float ds[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int i = 8 * c2 + e;
-            float p = fast_exp2(fminf(fmaf(s[i], scale_log2, -lse2), 0.f));
-            if constexpr (MASKED)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
+            float nb = -lse2;
+            if constexpr (HAS_MASK) {  // the mask's bias of key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g
+              const int key = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) + 4 * g;
+              nb = (key < Lkv ? mask_bias_log2<T>(mask.p, mask.kind, mrow + key) : -INFINITY) - lse2;
+            }
+            float p = fast_exp2(fminf(fmaf(s[i], scale_log2, nb), 0.f));
+            if constexpr (EDGE)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
               p = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) < klim ? p : 0.f;
             ds[e] = p * (dp[i] - dlt);
           }
@@ -271,7 +280,7 @@ constexpr int kv_waves() {
 }
 constexpr int kKvBM = 64;  // queries per tile
 
-template <typename T, int D, bool CAUSAL, typename OutT>
+template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
 __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_per_eu(kv_waves<D>() / 4, kv_waves<D>() / 4))) void dkv_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
                                                             const f32x2_t* __restrict__ rowstat,
                                                             OutT* __restrict__ dk, OutT* __restrict__ dv, int Hq,
                                                             int G, int Lq, int Lkv, int n_kblk, int n_bhk,
-                                                            int lq_pad, float scale_log2, float scale) {
+                                                            int lq_pad, float scale_log2, float scale, Mask mask) {
   using TL = SwzTile<D, 16>;
   constexpr int kKvWaves = kv_waves<D>();
   constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
@@ -357,7 +366,10 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   // One query tile. The LDS operand reads of each stage are issued one stage ahead of the
   // matrix-core instructions that use them; sched_fence() keeps the compiler from sinking
   // them back next to their uses.
-  auto tile = [&](bool masked, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0) {
+  // With a mask: element offset of (this tile's query head, query 0, key krow); rows are
+  // added per query (clamped into range: out-of-range entries are zeroed by the edge test).
+  const int64_t mkey = HAS_MASK ? (int64_t)b * mask.sb + (int64_t)min(krow, Lkv - 1) : 0;
+  auto tile = [&](bool masked, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0, int hq) {
     // Lane constants made opaque per tile, so that the compiler recomputes the LDS
     // addresses derived from them inside the loop instead of keeping each one live.
     int fa = fa0, ft = ft0, q4x4 = 4 * q4;
@@ -424,8 +436,8 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     // Only the softmax is duplicated for the masked case (a wave-uniform branch), so
     // both paths share the same registers.
     u32x4_t pop[2], dsop[2];
-    auto softmax = [&](auto masked_tag) {
-      constexpr bool MASKED = decltype(masked_tag)::value;
+    auto softmax = [&](auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         float pv[8], dsv[8];
@@ -435,8 +447,13 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
           const float l2[4] = {sa[qm][0], sa[qm][2], sb[qm][0], sb[qm][2]};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, -l2[j]), 0.f));
-            if constexpr (MASKED) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, sees key krow
+            float nb = -l2[j];
+            if constexpr (HAS_MASK) {  // bias of (query t0 + qm*16 + 4*q4 + j, key krow)
+              const int qi = min(t0 + qm * 16 + 4 * q4 + j, Lq - 1);
+              nb += mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh + (int64_t)qi * mask.sq);
+            }
+            float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, nb), 0.f));
+            if constexpr (EDGE) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, sees key krow
               const int u = t0 + qm * 16 + j + co;  // wave-uniform part
               p = (q4x4 < Lq + co - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
             }
@@ -483,7 +500,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = tile_of(it);
     if (CAUSAL && t0 + kKvBM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
-    tile((t0 + kKvBM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0);  // wave-uniform flag
+    tile((t0 + kKvBM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G);  // wave-uniform flag
   }
   if (krow < Lkv) {
     const int64_t ko = kvoff + (int64_t)krow * D;
@@ -496,10 +513,10 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   }
 }
 
-template <typename T, int D, bool C, typename OutT>
-hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                        const void* dO, void* dq, void* dk, void* dv, float* ws, float scale, int stages,
-                        hipStream_t st) {
+template <typename T, int D, bool C, bool M, typename OutT>
+hipError_t launch_typed(const Shape& s, const Mask& mask, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws, float scale,
+                        int stages, hipStream_t st) {
   f32x2_t* rowstat = (f32x2_t*)ws;  // [B*Hq][lq_pad] {LSE*log2e, Delta}
   const int lq_pad = (int)tiled_rowstat_stride(s.Lq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -507,9 +524,9 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
   if (stages & kStage0) {
     const int n_qblk = (int)((s.Lq + kDqBM - 1) / kDqBM);
     const int n_bh = (int)(s.B * s.Hq);
-    hipLaunchKernelGGL((dq_kernel<T, D, C, OutT>), dim3(n_qblk * n_bh), dim3(kThreads), 0, st, (const uint16_t*)q,
+    hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh), dim3(kThreads), 0, st, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse, (const uint16_t*)dO, (OutT*)dq,
-                       rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, lq_pad, scale_log2, scale);
+                       rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, lq_pad, scale_log2, scale, mask);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -517,44 +534,53 @@ hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void
   constexpr int kKvBN = 16 * kv_waves<D>();
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
-  hipLaunchKernelGGL((dkv_kernel<T, D, C, OutT>), dim3(n_kblk * n_bhk), dim3(64 * kv_waves<D>()), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, (const f32x2_t*)rowstat,
-                     (OutT*)dk, (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk, n_bhk, lq_pad, scale_log2,
-                     scale);
+  hipLaunchKernelGGL((dkv_kernel<T, D, C, M, OutT>), dim3(n_kblk * n_bhk), dim3(64 * kv_waves<D>()), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO,
+                     (const f32x2_t*)rowstat, (OutT*)dk, (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk,
+                     n_bhk, lq_pad, scale_log2, scale, mask);
   return hipGetLastError();
 }
 
+template <typename T, int D, typename OutT>
+hipError_t launch_mode(const Shape& s, bool causal, const Mask& mask, const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws,
+                       float scale, int stages, hipStream_t st) {
+  if (causal)
+    return launch_typed<T, D, true, false, OutT>(s, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
+  if (mask.kind != kMaskNone)
+    return launch_typed<T, D, false, true, OutT>(s, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
+  return launch_typed<T, D, false, false, OutT>(s, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
+}
+
 template <typename T, typename OutT>
-hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, const void* v, const void* o,
-                    const float* lse, const void* dO, void* dq, void* dk, void* dv, float* delta, float scale,
-                    int stages, hipStream_t st) {
-#define SDPA_BWD_CASE(DV)                                                                                          \
-  case DV:                                                                                                         \
-    return causal ? launch_typed<T, DV, true, OutT>(s, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st) \
-                  : launch_typed<T, DV, false, OutT>(s, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+hipError_t launch_d(const Shape& s, bool causal, const Mask& mask, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* delta,
+                    float scale, int stages, hipStream_t st) {
   switch (s.D) {
-    SDPA_BWD_CASE(32)
-    SDPA_BWD_CASE(64)
-    SDPA_BWD_CASE(96)
-    SDPA_BWD_CASE(128)
-    SDPA_BWD_CASE(256)
-    default:
-      return hipErrorInvalidValue;
+    case 32: return launch_mode<T, 32, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    case 64: return launch_mode<T, 64, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    case 96: return launch_mode<T, 96, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    case 128:
+      return launch_mode<T, 128, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    case 256:
+      return launch_mode<T, 256, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    default: return hipErrorInvalidValue;
   }
-#undef SDPA_BWD_CASE
 }
 
 }  // namespace
 
-hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                            float* delta, float scale, int stages, hipStream_t st) {
+hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
+                            const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+                            void* dk, void* dv, float* delta, float scale, int stages, hipStream_t st) {
   if (dt == kBF16)
-    return out == kF32 ? launch_d<bf16_t, float>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
-                       : launch_d<bf16_t, bf16_t>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    return out == kF32
+               ? launch_d<bf16_t, float>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
+               : launch_d<bf16_t, bf16_t>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
   if (dt == kF16)
-    return out == kF32 ? launch_d<f16_t, float>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
-                       : launch_d<f16_t, f16_t>(s, causal, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    return out == kF32
+               ? launch_d<f16_t, float>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
+               : launch_d<f16_t, f16_t>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
   return hipErrorInvalidValue;
 }
 

@@ -276,6 +276,17 @@ template <> struct Store4<f16_t> {
 
 // Load one element of an output-typed array as fp32.
 __device__ __forceinline__ float load_f32(const float* p) { return *p; }
+
+// The mask's additive bias in log2 units for element `off`: 0 or -inf for a boolean mask,
+// value * log2(e) for an additive one (operand type T: a 16-bit tag type or float).
+template <typename T>
+__device__ __forceinline__ float mask_bias_log2(const void* p, int kind, int64_t off) {
+  if (kind == 1) return ((const uint8_t*)p)[off] ? 0.f : -INFINITY;
+  if constexpr (sizeof(T) == 4)
+    return ((const float*)p)[off] * kLog2e;
+  else
+    return to_f32<T>(((const uint16_t*)p)[off]) * kLog2e;
+}
 __device__ __forceinline__ float load_f32(const bf16_t* p) { return to_f32<bf16_t>(p->bits); }
 __device__ __forceinline__ float load_f32(const f16_t* p) { return to_f32<f16_t>(p->bits); }
 

@@ -53,11 +53,12 @@ __device__ __forceinline__ float dot_slice(const float* x, const float* lds, int
   return acc;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool HAS_MASK>
 __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                                const float* __restrict__ v, float* __restrict__ o,
                                                                float* __restrict__ lse, int Hq, int G, int Lq,
-                                                               int Lkv, int n_qblk, float scale_log2) {
+                                                               int Lkv, int n_qblk, float scale_log2, Mask mask,
+                                                               const float* __restrict__ sinks) {
   using TL = F32Tile<D>;
   constexpr int R = TL::R, ROWS = kF32Threads / R;
   __shared__ float k_lds[TL::ELEMS];
@@ -74,6 +75,12 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  if (sinks != nullptr && sinks[hq] > -INFINITY) {  // the sink: a first key with no value
+    m = sinks[hq] * kLog2e;
+    l = 1.f;
+  }
+  const int64_t mrow =
+      HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
   const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
   const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS + co) : Lkv;
   for (int t0 = 0; t0 < kv_end; t0 += kF32BN) {
@@ -87,6 +94,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     for (int j = 0; j < kF32BN; ++j) {
       float x = row_sum<R>(dot_slice<D>(qv, k_lds, j, slice)) * scale_log2;
       const int key = t0 + j;
+      if (HAS_MASK && key < Lkv) x += mask_bias_log2<float>(mask.p, mask.kind, mrow + key);
       if (key >= Lkv || (CAUSAL && key > qrow + co)) x = -INFINITY;
       s[j] = x;
       tmax = fmaxf(tmax, x);
@@ -115,13 +123,13 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool HAS_MASK>
 __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                               const float* __restrict__ v, const float* __restrict__ lse,
                                                               const float* __restrict__ dO,
                                                               const float* __restrict__ delta, float* __restrict__ dq,
                                                               int Hq, int G, int Lq, int Lkv, int n_qblk,
-                                                              float scale_log2, float scale) {
+                                                              float scale_log2, float scale, Mask mask) {
   using TL = F32Tile<D>;
   constexpr int R = TL::R, ROWS = kF32Threads / R;
   __shared__ float k_lds[TL::ELEMS];
@@ -140,8 +148,11 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
     dov[e] = valid ? dO[roff + e] : 0.f;
     acc[e] = 0.f;
   }
-  const float lse2 = valid ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
+  float lse2 = valid ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
+  if (HAS_MASK && lse2 == -INFINITY) lse2 = INFINITY;  // a masked row with no key: P = 0
   const float dlt = valid ? delta[(int64_t)bh * Lq + qrow] : 0.f;
+  const int64_t mrow =
+      HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
   const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
   const int kv_end = CAUSAL ? min(Lkv, qblk * ROWS + ROWS + co) : Lkv;
   for (int t0 = 0; t0 < kv_end; t0 += kF32BN) {
@@ -154,7 +165,8 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
       const float sv = row_sum<R>(dot_slice<D>(qv, k_lds, j, slice));
       const float dp = row_sum<R>(dot_slice<D>(dov, v_lds, j, slice));
       const int key = t0 + j;
-      float p = fast_exp2(fminf(sv * scale_log2 - lse2, 0.f));
+      const float nb = HAS_MASK && key < Lkv ? mask_bias_log2<float>(mask.p, mask.kind, mrow + key) - lse2 : -lse2;
+      float p = fast_exp2(fminf(fmaf(sv, scale_log2, nb), 0.f));
       if (key >= Lkv || (CAUSAL && key > qrow + co)) p = 0.f;
       const float ds = p * (dp - dlt);
       const float* kr = k_lds + j * TL::PITCH + slice * TL::SP;
@@ -168,14 +180,14 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool HAS_MASK>
 __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                                const float* __restrict__ v,
                                                                const float* __restrict__ lse,
                                                                const float* __restrict__ dO,
                                                                const float* __restrict__ delta, float* __restrict__ dk,
                                                                float* __restrict__ dv, int Hq, int G, int Lq, int Lkv,
-                                                               int n_kblk, float scale_log2, float scale) {
+                                                               int n_kblk, float scale_log2, float scale, Mask mask) {
   using TL = F32Tile<D>;
   constexpr int R = TL::R, ROWS = kF32Threads / R;
   __shared__ float q_lds[TL::ELEMS];
@@ -207,7 +219,8 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
       TL::stage(do_lds, dO + qbase * D, t0, Lq);
       if (threadIdx.x < kF32BN) {
         const int i = t0 + threadIdx.x;
-        lse_lds[threadIdx.x] = (i < Lq) ? lse[qbase + i] * kLog2e : 0.f;
+        const float l2 = (i < Lq) ? lse[qbase + i] * kLog2e : 0.f;
+        lse_lds[threadIdx.x] = (HAS_MASK && l2 == -INFINITY) ? INFINITY : l2;  // no key: P = 0
         dl_lds[threadIdx.x] = (i < Lq) ? delta[qbase + i] : 0.f;
       }
       __syncthreads();
@@ -216,7 +229,12 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
         const int i = t0 + j;
         const float sv = row_sum<R>(dot_slice<D>(kv_, q_lds, j, slice));
         const float dp = row_sum<R>(dot_slice<D>(vv, do_lds, j, slice));
-        float p = fast_exp2(fminf(sv * scale_log2 - lse_lds[j], 0.f));
+        float nb = -lse_lds[j];
+        if constexpr (HAS_MASK)
+          nb += mask_bias_log2<float>(mask.p, mask.kind,
+                                      (int64_t)b * mask.sb + (int64_t)hq * mask.sh +
+                                          (int64_t)min(i, Lq - 1) * mask.sq + min(krow, Lkv - 1));
+        float p = fast_exp2(fminf(fmaf(sv, scale_log2, nb), 0.f));
         if (i >= Lq || (CAUSAL && krow > i + co)) p = 0.f;
         const float ds = p * (dp - dl_lds[j]);
         const float* qr = q_lds + j * TL::PITCH + slice * TL::SP;
@@ -238,64 +256,84 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
   }
 }
 
-template <int D, bool C>
-hipError_t fwd_typed(const Shape& s, const float* q, const float* k, const float* v, float* o, float* lse, float scale,
-                     hipStream_t st) {
+template <int D, bool C, bool M>
+hipError_t fwd_typed(const Shape& s, const Mask& mask, const float* sinks, const float* q, const float* k,
+                     const float* v, float* o, float* lse, float scale, hipStream_t st) {
   constexpr int ROWS = kF32Threads / F32Tile<D>::R;
   const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, o, lse,
-                     (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk,
-                     (float)((double)scale * 1.4426950408889634));
+  hipLaunchKernelGGL((fwd_f32_kernel<D, C, M>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, o,
+                     lse, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk,
+                     (float)((double)scale * 1.4426950408889634), mask, sinks);
   return hipGetLastError();
 }
 
-template <int D, bool C>
-hipError_t bwd_typed(const Shape& s, const float* q, const float* k, const float* v, const float* lse,
-                     const float* dO, const float* delta, float* dq, float* dk, float* dv, float scale, int stages,
-                     hipStream_t st) {
+template <int D, bool C, bool M>
+hipError_t bwd_typed(const Shape& s, const Mask& mask, const float* q, const float* k, const float* v,
+                     const float* lse, const float* dO, const float* delta, float* dq, float* dk, float* dv,
+                     float scale, int stages, hipStream_t st) {
   constexpr int ROWS = kF32Threads / F32Tile<D>::R;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (stages & kStage0) {
     const int n_qblk = (int)((s.Lq + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((dq_f32_kernel<D, C>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
-                       delta, dq, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, scale_log2, scale);
+    hipLaunchKernelGGL((dq_f32_kernel<D, C, M>), dim3(n_qblk * s.B * s.Hq), dim3(kF32Threads), 0, st, q, k, v, lse,
+                       dO, delta, dq, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, scale_log2,
+                       scale, mask);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(stages & kStage1)) return hipSuccess;
   const int n_kblk = (int)((s.Lkv + ROWS - 1) / ROWS);
-  hipLaunchKernelGGL((dkv_f32_kernel<D, C>), dim3(n_kblk * s.B * s.Hkv), dim3(kF32Threads), 0, st, q, k, v, lse, dO,
-                     delta, dk, dv, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_kblk, scale_log2, scale);
+  hipLaunchKernelGGL((dkv_f32_kernel<D, C, M>), dim3(n_kblk * s.B * s.Hkv), dim3(kF32Threads), 0, st, q, k, v, lse,
+                     dO, delta, dk, dv, (int)s.Hq, (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_kblk, scale_log2,
+                     scale, mask);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t fwd_mode(const Shape& s, bool causal, const Mask& mask, const float* sinks, const float* q, const float* k,
+                    const float* v, float* o, float* lse, float scale, hipStream_t st) {
+  if (causal) return fwd_typed<D, true, false>(s, mask, sinks, q, k, v, o, lse, scale, st);
+  if (mask.kind != kMaskNone) return fwd_typed<D, false, true>(s, mask, sinks, q, k, v, o, lse, scale, st);
+  return fwd_typed<D, false, false>(s, mask, sinks, q, k, v, o, lse, scale, st);
+}
+
+template <int D>
+hipError_t bwd_mode(const Shape& s, bool causal, const Mask& mask, const float* q, const float* k, const float* v,
+                    const float* lse, const float* dO, const float* delta, float* dq, float* dk, float* dv,
+                    float scale, int stages, hipStream_t st) {
+  if (causal) return bwd_typed<D, true, false>(s, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+  if (mask.kind != kMaskNone)
+    return bwd_typed<D, false, true>(s, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+  return bwd_typed<D, false, false>(s, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v, float* o,
-                          float* lse, float scale, hipStream_t st) {
+hipError_t launch_fwd_f32(const Shape& s, bool causal, const Mask& mask, const float* sinks, const float* q,
+                          const float* k, const float* v, float* o, float* lse, float scale, hipStream_t st) {
   switch (s.D) {
-    case 32: return causal ? fwd_typed<32, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<32, false>(s, q, k, v, o, lse, scale, st);
-    case 64: return causal ? fwd_typed<64, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<64, false>(s, q, k, v, o, lse, scale, st);
-    case 96: return causal ? fwd_typed<96, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<96, false>(s, q, k, v, o, lse, scale, st);
-    case 128: return causal ? fwd_typed<128, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<128, false>(s, q, k, v, o, lse, scale, st);
-    case 256: return causal ? fwd_typed<256, true>(s, q, k, v, o, lse, scale, st) : fwd_typed<256, false>(s, q, k, v, o, lse, scale, st);
+    case 32: return fwd_mode<32>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 64: return fwd_mode<64>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 96: return fwd_mode<96>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 128: return fwd_mode<128>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 256: return fwd_mode<256>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v,
-                          const float* o, const float* lse, const float* dO, float* dq, float* dk, float* dv,
-                          float* delta, float scale, int stages, hipStream_t st) {
+hipError_t launch_bwd_f32(const Shape& s, bool causal, const Mask& mask, const float* q, const float* k,
+                          const float* v, const float* o, const float* lse, const float* dO, float* dq, float* dk,
+                          float* dv, float* delta, float scale, int stages, hipStream_t st) {
   if (stages & kStage0) {
     hipError_t e = launch_delta(s, kF32, kF32, o, dO, delta, st);
     if (e != hipSuccess) return e;
   }
   switch (s.D) {
-    case 32: return causal ? bwd_typed<32, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<32, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
-    case 64: return causal ? bwd_typed<64, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<64, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
-    case 96: return causal ? bwd_typed<96, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<96, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
-    case 128: return causal ? bwd_typed<128, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<128, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
-    case 256: return causal ? bwd_typed<256, true>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st) : bwd_typed<256, false>(s, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 32: return bwd_mode<32>(s, causal, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 64: return bwd_mode<64>(s, causal, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 96: return bwd_mode<96>(s, causal, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 128: return bwd_mode<128>(s, causal, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
+    case 256: return bwd_mode<256>(s, causal, mask, q, k, v, lse, dO, delta, dq, dk, dv, scale, stages, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,6 +21,12 @@
 // half-wave exchange, the rescale factor is per lane, and the probabilities
 // already sit in the B-operand layout of O^T += V^T P^T. V^T is read from the
 // row-major V tile with the LDS transpose read.
+//
+// Masks and sinks (MASKED instantiations; the sink is a runtime pointer): the mask's
+// bias enters every score in the log2 domain before the row maximum, and a row's sink
+// logit seeds the reference maximum and the row sum as if it were a first key with no
+// value (the drop-in semantics that mps-flash-sdpa 0.1.0, "When MFA Dispatches vs.
+// Falls Back", and the MLX pull request, "Limitations", leave to the unfused path).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,11 +42,11 @@ constexpr int fwd_bn() {
   return D == 256 ? 32 : 64;
 }
 
-template <typename T, int D, bool CAUSAL, typename OutT>
+template <typename T, int D, bool CAUSAL, bool MASKED, typename OutT>
 __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     OutT* __restrict__ o, float* __restrict__ lse, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
-    float scale_log2) {
+    float scale_log2, Mask mask, const float* __restrict__ sinks) {
   using TL = SwzTile<D>;
   constexpr int kFwdBN = fwd_bn<D>();
   constexpr int TILE = kFwdBN * TL::RB;  // bytes of one K or V tile
@@ -77,6 +83,17 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = -INFINITY;  // reference row max of the log2-domain scores (see kRescaleSlack)
   float lsum = 0.f;     // this lane's share of the running row sum
+  if (sinks != nullptr) {  // the sink: a first "key" of score sink*log2e and no value
+    const float sk = sinks[hq] * kLog2e;
+    if (sk > -INFINITY) {
+      m = sk;
+      lsum = g == 0 ? 1.f : 0.f;
+    }
+  }
+  // With a mask the scores are moved to the log2 domain (scale and bias) before the row
+  // maximum, and the remaining steps take them with unit scale.
+  const float sl2 = MASKED ? 1.f : scale_log2;
+  const int64_t mrow = MASKED ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
 
   // Causal: key j is visible to query i iff j <= i + co, co = Lkv - Lq >= 0 (sequences
   // aligned at their ends; co = 0 when the lengths are equal).
@@ -126,8 +143,17 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
         s[kb] = mfma32<T>(a, qop[c], s[kb]);
       }
 
-    // Mask (only tiles that reach past the diagonal or the end), then the row max on raw scores.
-    if ((kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0 + co)) {
+    if constexpr (MASKED) {  // every tile: s <- s*scale*log2e + bias, keys past the end -inf
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          s[kb][i] = key < Lkv ? fmaf(s[kb][i], scale_log2, mask_bias_log2<T>(mask.p, mask.kind, mrow + key))
+                               : -INFINITY;
+        }
+    } else if ((kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0 + co)) {
+      // Mask (only tiles that reach past the diagonal or the end), then the row max on raw scores.
 #pragma unroll
       for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
@@ -141,12 +167,14 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-    tmax = half_swap_max(tmax) * scale_log2;
+    tmax = half_swap_max(tmax) * sl2;
     // Raise the reference max only past the slack; rescale O when any row of the wave moved.
     const bool grow = tmax > m + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? tmax : m;
-      const float alpha = fast_exp2(m - m_new);
+      // A row that did not move keeps its scale (with a mask its m may still be -inf,
+      // where m - m_new would be NaN).
+      const float alpha = (MASKED && !grow) ? 1.f : fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
 #pragma unroll
@@ -165,7 +193,7 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(s[kb][8 * c2 + e], scale_log2, neg_m));
+          p[e] = fast_exp2(fmaf(s[kb][8 * c2 + e], sl2, neg_m));
           lsum += p[e];
         }
         const u32x4_t pop = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
@@ -195,52 +223,50 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
   }
 }
 
-template <typename T, int D, bool C, typename OutT>
-hipError_t launch_typed(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse, float scale,
-                        hipStream_t st) {
+template <typename T, int D, bool C, bool M, typename OutT>
+hipError_t launch_typed(const Shape& s, const Mask& mask, const float* sinks, const void* q, const void* k,
+                        const void* v, void* o, float* lse, float scale, hipStream_t st) {
   const int n_qblk = (int)((s.Lq + kFwdBM - 1) / kFwdBM);
   const int n_bh = (int)(s.B * s.Hq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, OutT>), dim3(n_qblk * n_bh), dim3(kFwdThreads), 0, st,
+  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh), dim3(kFwdThreads), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, (int)s.Hq,
-                     (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2);
+                     (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, mask, sinks);
   return hipGetLastError();
 }
 
+template <typename T, int D, typename OutT>
+hipError_t launch_mode(const Shape& s, bool causal, const Mask& mask, const float* sinks, const void* q,
+                       const void* k, const void* v, void* o, float* lse, float scale, hipStream_t st) {
+  if (causal) return launch_typed<T, D, true, false, OutT>(s, mask, sinks, q, k, v, o, lse, scale, st);
+  if (mask.kind != kMaskNone) return launch_typed<T, D, false, true, OutT>(s, mask, sinks, q, k, v, o, lse, scale, st);
+  return launch_typed<T, D, false, false, OutT>(s, mask, sinks, q, k, v, o, lse, scale, st);
+}
+
 template <typename T, typename OutT>
-hipError_t launch_d(const Shape& s, bool causal, const void* q, const void* k, const void* v, void* o, float* lse,
-                    float scale, hipStream_t st) {
+hipError_t launch_d(const Shape& s, bool causal, const Mask& mask, const float* sinks, const void* q, const void* k,
+                    const void* v, void* o, float* lse, float scale, hipStream_t st) {
   switch (s.D) {
-    case 32:
-      return causal ? launch_typed<T, 32, true, OutT>(s, q, k, v, o, lse, scale, st)
-                    : launch_typed<T, 32, false, OutT>(s, q, k, v, o, lse, scale, st);
-    case 64:
-      return causal ? launch_typed<T, 64, true, OutT>(s, q, k, v, o, lse, scale, st)
-                    : launch_typed<T, 64, false, OutT>(s, q, k, v, o, lse, scale, st);
-    case 96:
-      return causal ? launch_typed<T, 96, true, OutT>(s, q, k, v, o, lse, scale, st)
-                    : launch_typed<T, 96, false, OutT>(s, q, k, v, o, lse, scale, st);
-    case 128:
-      return causal ? launch_typed<T, 128, true, OutT>(s, q, k, v, o, lse, scale, st)
-                    : launch_typed<T, 128, false, OutT>(s, q, k, v, o, lse, scale, st);
-    case 256:
-      return causal ? launch_typed<T, 256, true, OutT>(s, q, k, v, o, lse, scale, st)
-                    : launch_typed<T, 256, false, OutT>(s, q, k, v, o, lse, scale, st);
-    default:
-      return hipErrorInvalidValue;
+    case 32: return launch_mode<T, 32, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 64: return launch_mode<T, 64, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 96: return launch_mode<T, 96, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 128: return launch_mode<T, 128, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 256: return launch_mode<T, 256, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                            void* o, float* lse, float scale, hipStream_t st) {
+hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
+                            const void* q, const void* k, const void* v, void* o, float* lse, float scale,
+                            hipStream_t st) {
   if (dt == kBF16)
-    return out == kF32 ? launch_d<bf16_t, float>(s, causal, q, k, v, o, lse, scale, st)
-                       : launch_d<bf16_t, bf16_t>(s, causal, q, k, v, o, lse, scale, st);
+    return out == kF32 ? launch_d<bf16_t, float>(s, causal, mask, sinks, q, k, v, o, lse, scale, st)
+                       : launch_d<bf16_t, bf16_t>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
   if (dt == kF16)
-    return out == kF32 ? launch_d<f16_t, float>(s, causal, q, k, v, o, lse, scale, st)
-                       : launch_d<f16_t, f16_t>(s, causal, q, k, v, o, lse, scale, st);
+    return out == kF32 ? launch_d<f16_t, float>(s, causal, mask, sinks, q, k, v, o, lse, scale, st)
+                       : launch_d<f16_t, f16_t>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
   return hipErrorInvalidValue;
 }
 

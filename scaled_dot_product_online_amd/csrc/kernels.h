@@ -17,36 +17,57 @@ struct Shape {
 // Backward stages (bit mask): stage 0 and stage 1 as documented for sdpa_bwd_stage.
 enum { kStage0 = 1, kStage1 = 2, kStagesAll = 3 };
 
+// Attention mask as the kernels read it (validated by the caller). Element (b, h, i, j)
+// sits at p + b*sb + h*sh + i*sq + j elements; a stride of 0 broadcasts. kind: boolean
+// bytes (nonzero keeps the key) or additive values in the operand type. A mask is never
+// combined with causal masking.
+enum { kMaskNone = 0, kMaskBool = 1, kMaskAdd = 2 };
+struct Mask {
+  const void* p;
+  int kind;
+  int64_t sb, sh, sq;
+};
+constexpr Mask kNoMask = {nullptr, kMaskNone, 0, 0, 0};
+
+// dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * Delta(b,h,i), with Delta(b,h,i) at
+// delta[((b*Hq + h) * pitch + i) * es] (delta.hip). One deterministic reduction per head.
+hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es,
+                            const float* sinks, float* dsinks, hipStream_t st);
+
 // Delta_i = sum_d dO[i,d] * O[i,d] over all B*Hq*Lq rows (delta.hip).
 hipError_t launch_delta(const Shape& s, Dt o_dt, Dt do_dt, const void* o, const void* dO, float* delta,
                         hipStream_t st);
 
 // Tiled forward, 16-bit operands (fwd_tiled.hip).
-hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                            void* o, float* lse, float scale, hipStream_t st);
+hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
+                            const void* q, const void* k, const void* v, void* o, float* lse, float scale,
+                            hipStream_t st);
 
 // Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is the workspace: per (b, hq)
 // a row of tiled_rowstat_stride(Lq) {LSE*log2e, Delta} fp32 pairs.
 inline int64_t tiled_rowstat_stride(int64_t Lq) { return (Lq + 63) / 64 * 64; }
-hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
-                            float* delta, float scale, int stages, hipStream_t st);
+hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
+                            const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+                            void* dk, void* dv, float* delta, float scale, int stages, hipStream_t st);
 
 // float32 path (fp32_path.hip).
-hipError_t launch_fwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v, float* o,
-                          float* lse, float scale, hipStream_t st);
-hipError_t launch_bwd_f32(const Shape& s, bool causal, const float* q, const float* k, const float* v,
-                          const float* o, const float* lse, const float* dO, float* dq, float* dk, float* dv,
-                          float* delta, float scale, int stages, hipStream_t st);
+hipError_t launch_fwd_f32(const Shape& s, bool causal, const Mask& mask, const float* sinks, const float* q,
+                          const float* k, const float* v, float* o, float* lse, float scale, hipStream_t st);
+hipError_t launch_bwd_f32(const Shape& s, bool causal, const Mask& mask, const float* q, const float* k,
+                          const float* v, const float* o, const float* lse, const float* dO, float* dq, float* dk,
+                          float* dv, float* delta, float scale, int stages, hipStream_t st);
 
 // Short-query path (vector_path.hip).
 int vector_num_splits(const Shape& s);
 size_t vector_fwd_workspace(const Shape& s);
 size_t vector_bwd_workspace(const Shape& s);
-hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                             void* o, float* lse, float scale, void* ws, hipStream_t st);
-hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
-                             float scale, int stages, hipStream_t st);
+// Offset (bytes) in the vector backward's workspace of its Delta array [B*Hq*Lq] fp32.
+size_t vector_bwd_delta_offset(const Shape& s);
+hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
+                             const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,
+                             hipStream_t st);
+hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
+                             const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+                             void* dk, void* dv, void* ws, float scale, int stages, hipStream_t st);
 
 }  // namespace sdpa

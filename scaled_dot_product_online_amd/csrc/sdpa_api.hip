@@ -67,6 +67,64 @@ size_t ws_bytes(int backward, const Shape& s, int path) {
 
 sdpa_status_t device_status(hipError_t e) { return e == hipSuccess ? SDPA_OK : SDPA_ERR_DEVICE; }
 
+// Mask arguments of the *_masked entry points; fills `m` for the kernels.
+sdpa_status_t check_mask(int kind, const void* mask, int64_t sb, int64_t sh, int64_t sq, int64_t B, int64_t Hq,
+                         int64_t Lq, int64_t Lkv, int is_causal, int dtype, sdpa::Mask* m) {
+  *m = sdpa::kNoMask;
+  if (kind == SDPA_MASK_NONE) return SDPA_OK;
+  if (kind != SDPA_MASK_BOOL && kind != SDPA_MASK_ADDITIVE) return SDPA_ERR_VALUE;
+  if (is_causal) return SDPA_ERR_UNSUPPORTED;
+  if (!mask) return SDPA_ERR_NULL;
+  if (sb < 0 || sh < 0 || sq < 0) return SDPA_ERR_SHAPE;
+  // Largest element offset: (B-1)*sb + (Hq-1)*sh + (Lq-1)*sq + Lkv - 1, in int64.
+  int64_t t0, t1, t2, last;
+  if (__builtin_mul_overflow(B - 1, sb, &t0) || __builtin_mul_overflow(Hq - 1, sh, &t1) ||
+      __builtin_mul_overflow(Lq - 1, sq, &t2) || __builtin_add_overflow(t0, t1, &last) ||
+      __builtin_add_overflow(last, t2, &last) || __builtin_add_overflow(last, Lkv, &last) ||
+      last > (INT64_MAX >> 3))
+    return SDPA_ERR_SHAPE;
+  const uintptr_t esz = kind == SDPA_MASK_BOOL ? 1 : (dtype == SDPA_F32 ? 4 : 2);
+  if (((uintptr_t)mask & (esz - 1)) != 0) return SDPA_ERR_ALIGN;
+  *m = sdpa::Mask{mask, kind == SDPA_MASK_BOOL ? sdpa::kMaskBool : sdpa::kMaskAdd, sb, sh, sq};
+  return SDPA_OK;
+}
+
+sdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                      int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal, int mask_kind,
+                      const void* mask_p, int64_t msb, int64_t msh, int64_t msq, const float* sinks,
+                      sdpa_dtype_t dtype, sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  sdpa_status_t st = check_shape(B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype, out_dtype);
+  if (st != SDPA_OK) return st;
+  if (!isfinite(scale)) return SDPA_ERR_VALUE;
+  sdpa::Mask mask;
+  st = check_mask(mask_kind, mask_p, msb, msh, msq, B, Hq, Lq, Lkv, is_causal, dtype, &mask);
+  if (st != SDPA_OK) return st;
+  if (!q || !k || !v || !o) return SDPA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SDPA_ERR_ALIGN;
+  if (((uintptr_t)sinks & 3u) != 0) return SDPA_ERR_ALIGN;
+  const Shape s{B, Hq, Hkv, Lq, Lkv, D};
+  const int path = path_of(Hq, Hkv, Lq, is_causal, dtype);
+  const size_t need = ws_bytes(0, s, path);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return SDPA_ERR_ALIGN;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  const bool causal = is_causal != 0;
+  switch (path) {
+    case SDPA_PATH_FP32:
+      return device_status(sdpa::launch_fwd_f32(s, causal, mask, sinks, (const float*)q, (const float*)k,
+                                                (const float*)v, (float*)o, lse, scale, hs));
+    case SDPA_PATH_VECTOR:
+      return device_status(sdpa::launch_fwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, mask, sinks, q, k,
+                                                   v, o, lse, scale, workspace, hs));
+    default:
+      return device_status(sdpa::launch_fwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, mask, sinks, q, k,
+                                                  v, o, lse, scale, hs));
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -87,31 +145,17 @@ sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal,
                        sdpa_dtype_t dtype, sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  sdpa_status_t st = check_shape(B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype, out_dtype);
-  if (st != SDPA_OK) return st;
-  if (!isfinite(scale)) return SDPA_ERR_VALUE;
-  if (!q || !k || !v || !o) return SDPA_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return SDPA_ERR_ALIGN;
-  const Shape s{B, Hq, Hkv, Lq, Lkv, D};
-  const int path = path_of(Hq, Hkv, Lq, is_causal, dtype);
-  const size_t need = ws_bytes(0, s, path);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
-    if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return SDPA_ERR_ALIGN;
-  }
-  hipStream_t hs = (hipStream_t)stream;
-  const bool causal = is_causal != 0;
-  switch (path) {
-    case SDPA_PATH_FP32:
-      return device_status(sdpa::launch_fwd_f32(s, causal, (const float*)q, (const float*)k, (const float*)v,
-                                                (float*)o, lse, scale, hs));
-    case SDPA_PATH_VECTOR:
-      return device_status(sdpa::launch_fwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse, scale,
-                                                   workspace, hs));
-    default:
-      return device_status(
-          sdpa::launch_fwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse, scale, hs));
-  }
+  return run_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal, SDPA_MASK_NONE, nullptr, 0, 0, 0, nullptr,
+                 dtype, out_dtype, workspace, workspace_bytes, stream);
+}
+
+sdpa_status_t sdpa_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+                              int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal,
+                              sdpa_mask_kind_t mask_kind, const void* mask, int64_t mask_stride_b,
+                              int64_t mask_stride_h, int64_t mask_stride_q, const float* sinks, sdpa_dtype_t dtype,
+                              sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_fwd(q, k, v, o, lse, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal, mask_kind, mask, mask_stride_b,
+                 mask_stride_h, mask_stride_q, sinks, dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -120,12 +164,18 @@ namespace {
 
 sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq,
-                      int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      int64_t Lkv, int64_t D, float scale, int is_causal, int mask_kind, const void* mask_p,
+                      int64_t msb, int64_t msh, int64_t msq, const float* sinks, float* dsinks, sdpa_dtype_t dtype,
+                      sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   sdpa_status_t st = check_shape(B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype, out_dtype);
   if (st != SDPA_OK) return st;
   if (!isfinite(scale)) return SDPA_ERR_VALUE;
+  sdpa::Mask mask;
+  st = check_mask(mask_kind, mask_p, msb, msh, msq, B, Hq, Lq, Lkv, is_causal, dtype, &mask);
+  if (st != SDPA_OK) return st;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return SDPA_ERR_NULL;
+  if (sinks && !dsinks) return SDPA_ERR_NULL;
+  if (((uintptr_t)sinks & 3u) != 0 || ((uintptr_t)dsinks & 3u) != 0) return SDPA_ERR_ALIGN;
   const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SDPA_ERR_ALIGN;
@@ -137,18 +187,31 @@ sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, c
   hipStream_t hs = (hipStream_t)stream;
   const bool causal = is_causal != 0;
   float* delta = (float*)workspace;
+  hipError_t e;
+  // Where stage 0 leaves Delta_i for the sinks' gradient: element (bh * pitch + i) * es.
+  const float* dl;
+  int64_t pitch;
+  int es;
   switch (path) {
     case SDPA_PATH_FP32:
-      return device_status(sdpa::launch_bwd_f32(s, causal, (const float*)q, (const float*)k, (const float*)v,
-                                                (const float*)o, lse, (const float*)dO, (float*)dq, (float*)dk,
-                                                (float*)dv, delta, scale, stages, hs));
+      e = sdpa::launch_bwd_f32(s, causal, mask, (const float*)q, (const float*)k, (const float*)v, (const float*)o,
+                               lse, (const float*)dO, (float*)dq, (float*)dk, (float*)dv, delta, scale, stages, hs);
+      dl = delta, pitch = Lq, es = 1;
+      break;
     case SDPA_PATH_VECTOR:
-      return device_status(sdpa::launch_bwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse, dO, dq,
-                                                   dk, dv, workspace, scale, stages, hs));
+      e = sdpa::launch_bwd_vector(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, mask, q, k, v, o, lse, dO, dq, dk,
+                                  dv, workspace, scale, stages, hs);
+      dl = (const float*)((const char*)workspace + sdpa::vector_bwd_delta_offset(s)), pitch = Lq, es = 1;
+      break;
     default:
-      return device_status(sdpa::launch_bwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, q, k, v, o, lse,
-                                                  dO, dq, dk, dv, delta, scale, stages, hs));
+      e = sdpa::launch_bwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, mask, q, k, v, o, lse, dO, dq, dk,
+                                 dv, delta, scale, stages, hs);
+      dl = delta + 1, pitch = sdpa::tiled_rowstat_stride(Lq), es = 2;  // {LSE*log2e, Delta} pairs
+      break;
   }
+  if (e == hipSuccess && sinks && (stages & sdpa::kStage1))
+    e = sdpa::launch_sink_grad(s, lse, dl, pitch, es, sinks, dsinks, hs);
+  return device_status(e);
 }
 
 }  // namespace
@@ -159,8 +222,21 @@ sdpa_status_t sdpa_bwd(const void* q, const void* k, const void* v, const void* 
                        void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
                        int64_t D, float scale, int is_causal, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return run_bwd(sdpa::kStagesAll, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal, dtype,
-                 out_dtype, workspace, workspace_bytes, stream);
+  return run_bwd(sdpa::kStagesAll, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal,
+                 SDPA_MASK_NONE, nullptr, 0, 0, 0, nullptr, nullptr, dtype, out_dtype, workspace, workspace_bytes,
+                 stream);
+}
+
+sdpa_status_t sdpa_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal,
+                              sdpa_mask_kind_t mask_kind, const void* mask, int64_t mask_stride_b,
+                              int64_t mask_stride_h, int64_t mask_stride_q, const float* sinks, float* dsinks,
+                              sdpa_dtype_t dtype, sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return run_bwd(sdpa::kStagesAll, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal,
+                 mask_kind, mask, mask_stride_b, mask_stride_h, mask_stride_q, sinks, dsinks, dtype, out_dtype,
+                 workspace, workspace_bytes, stream);
 }
 
 sdpa_status_t sdpa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -169,7 +245,8 @@ sdpa_status_t sdpa_bwd_stage(int stage, const void* q, const void* k, const void
                              sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (stage != 0 && stage != 1) return SDPA_ERR_VALUE;
   return run_bwd(stage == 0 ? sdpa::kStage0 : sdpa::kStage1, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
-                 scale, is_causal, dtype, out_dtype, workspace, workspace_bytes, stream);
+                 scale, is_causal, SDPA_MASK_NONE, nullptr, 0, 0, 0, nullptr, nullptr, dtype, out_dtype, workspace,
+                 workspace_bytes, stream);
 }
 
 const char* sdpa_status_str(sdpa_status_t status) {
@@ -177,11 +254,11 @@ const char* sdpa_status_str(sdpa_status_t status) {
     case SDPA_OK: return "ok";
     case SDPA_ERR_NULL: return "a required pointer is NULL";
     case SDPA_ERR_SHAPE: return "invalid shape (size < 1, Hq not a multiple of Hkv, or too large)";
-    case SDPA_ERR_UNSUPPORTED: return "unsupported combination (head dim, dtype, or causal with Lq != Lkv)";
+    case SDPA_ERR_UNSUPPORTED: return "unsupported combination (head dim, dtype, causal with Lq > Lkv or with a mask)";
     case SDPA_ERR_WORKSPACE: return "workspace missing or smaller than sdpa_workspace_bytes()";
     case SDPA_ERR_ALIGN: return "pointer not 16-byte aligned (workspace: 256-byte)";
     case SDPA_ERR_DEVICE: return "HIP runtime rejected a kernel launch";
-    case SDPA_ERR_VALUE: return "scale is not finite";
+    case SDPA_ERR_VALUE: return "scale is not finite, or an invalid stage number or mask kind";
     default: return "unknown status";
   }
 }

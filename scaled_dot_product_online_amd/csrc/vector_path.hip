@@ -69,14 +69,15 @@ SplitPlan plan(const Shape& s) {
   return SplitPlan{(int)((s.Lkv + len - 1) / len), len};
 }
 
-template <typename T, int D, bool CAUSAL, typename OutT>
+template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
 __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, OutT* __restrict__ o,
                                                               float* __restrict__ lse, float* __restrict__ part_o,
                                                               float* __restrict__ part_ml, int Hq, int G, int Lq,
                                                               int Lkv, int nsplit, int split_len, int n_rb,
-                                                              int64_t total_rows, float scale_log2) {
+                                                              int64_t total_rows, float scale_log2, Mask mask,
+                                                              const float* __restrict__ sinks) {
   using TL = SwzTile<D>;
   constexpr int kWaves = vec_waves<D>();
   constexpr int TILE = kVecKeys * TL::RB;         // bytes of one K or V tile
@@ -109,6 +110,13 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
   // Causal (sequences aligned at their ends): packed row r is query r % Lq of its head
   // and sees keys up to (r % Lq) + Lkv - Lq.
   const int qlim = CAUSAL ? (rb * 32 + n) % Lq + (Lkv - Lq) : Lkv;
+  // With a mask: element offset of packed row rb*32 + n (head hk*G + row / Lq, query
+  // row % Lq; rows past the group clamped into range, their outputs are not stored).
+  int64_t mrow = 0;
+  if constexpr (HAS_MASK) {
+    const int r = min(rb * 32 + n, rows - 1);
+    mrow = (int64_t)b * mask.sb + (int64_t)(hk * G + r / Lq) * mask.sh + (int64_t)(r % Lq) * mask.sq;
+  }
   // This wave's contiguous key segment [kb0, kb1).
   const int seg = split_len / kWaves;
   const int kb0 = split * split_len + wave * seg;
@@ -180,7 +188,12 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[i] *= scale_log2;
+      if constexpr (HAS_MASK) {  // scale and the mask's bias, keys past the segment stay -inf
+        const int key = min(t0 + 8 * (i >> 2) + 4 * g + (i & 3), Lkv - 1);
+        s[i] = fmaf(s[i], scale_log2, mask_bias_log2<T>(mask.p, mask.kind, mrow + key));
+      } else {
+        s[i] *= scale_log2;
+      }
       tmax = fmaxf(tmax, s[i]);
     }
     tmax = half_swap_max(tmax);
@@ -241,14 +254,17 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
   constexpr int TPM = 2 * kWaves;
   const int mr = tid / TPM, part = tid % TPM;
   const int rr = rb * 32 + mr;
-  float mw[kWaves], M = -INFINITY;
+  // The sink joins the row here when there is one split, else in the combine kernel.
+  const float sk =
+      (nsplit == 1 && sinks != nullptr && rr < rows) ? sinks[hk * G + rr / Lq] * kLog2e : -INFINITY;
+  float mw[kWaves], M = sk;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     mw[w] = mrg_m[w][mr];
     M = fmaxf(M, mw[w]);
   }
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float sc[kWaves], L = 0.f;
+  float sc[kWaves], L = sk > -INFINITY ? fast_exp2(sk - Mu) : 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     sc[w] = fast_exp2(mw[w] - Mu);
@@ -295,17 +311,20 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __restrict__ part_o,
                                                                const float* __restrict__ part_ml,
                                                                OutT* __restrict__ o, float* __restrict__ lse,
-                                                               int64_t total_rows, int nsplit) {
+                                                               int64_t total_rows, int nsplit,
+                                                               const float* __restrict__ sinks, int Hq, int Lq) {
   constexpr int TPR = D / 4;            // threads per row, 4 columns each
   constexpr int RPB = kThreads / TPR;  // rows per block (D = 96: 10 rows, 16 threads idle)
   if ((int)threadIdx.x >= RPB * TPR) return;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 4;
   if (row >= total_rows) return;
-  float M = -INFINITY;
+  // The sink of the row's query head: one more term of the denominator, with no value.
+  const float sk = sinks != nullptr ? sinks[(row / Lq) % Hq] * kLog2e : -INFINITY;
+  float M = sk;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((int64_t)s * total_rows + row) * 2]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+  float L = sk > -INFINITY ? fast_exp2(sk - Mu) : 0.f, x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const int64_t pr = (int64_t)s * total_rows + row;
     const float w = fast_exp2(part_ml[pr * 2] - Mu);
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void vec_combine_kernel(const float* __re
 // the dS^T scratch lives in the step's V tile once dP has consumed it, the per-row
 // statistics are kept in registers, and dV/dK are formed in two halves of d after the
 // dQ update, each staged as soon as it is complete.
-template <typename T, int D, bool CAUSAL, typename OutT>
+template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
 __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
@@ -343,7 +362,7 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
                                                               OutT* __restrict__ dv, float* __restrict__ dq_part,
                                                               int Hq, int G, int Lq, int Lkv, int nsplit,
                                                               int split_len, int64_t total_rows, float scale_log2,
-                                                              float scale) {
+                                                              float scale, Mask mask, float* __restrict__ delta_out) {
   using TL = SwzTile<D>;
   constexpr int kWaves = vec_waves<D>();
   constexpr int kWgThreads = 64 * kWaves;
@@ -390,8 +409,10 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
     for (int off = 1; off < TPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
     if (part == 0) {
       dl_lds[r] = acc;
-      lse_lds[r] = (r < rows) ? lse[row0 + r] * kLog2e : 0.f;
+      const float l2 = (r < rows) ? lse[row0 + r] * kLog2e : 0.f;
+      lse_lds[r] = (HAS_MASK && l2 == -INFINITY) ? INFINITY : l2;  // a masked row with no key: P = 0
       lim_lds[r] = CAUSAL ? r % Lq + (Lkv - Lq) : Lkv;
+      if (delta_out != nullptr && split == 0 && r < rows) delta_out[row0 + r] = acc;  // for the sinks' gradient
     }
     wait_vmem();
     __syncthreads();
@@ -493,7 +514,14 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 8 * c2 + 4 * h + j;
-          float p = fast_exp2(fminf(s[i] * scale_log2 - l4[j], 0.f));
+          float nb = -l4[j];
+          if constexpr (HAS_MASK) {  // bias of (packed row r0 + j, key), both clamped into range
+            const int r = min(r0 + j, rows - 1);
+            nb += mask_bias_log2<T>(mask.p, mask.kind,
+                                    (int64_t)b * mask.sb + (int64_t)(hk * G + r / Lq) * mask.sh +
+                                        (int64_t)(r % Lq) * mask.sq + min(key, Lkv - 1));
+          }
+          float p = fast_exp2(fminf(fmaf(s[i], scale_log2, nb), 0.f));
           if (r0 + j >= rows || key >= kb1 || (CAUSAL && key > lim4[j])) p = 0.f;
           pv[4 * h + j] = p;
           dsv[4 * h + j] = p * (dp[i] - d4[j]);
@@ -655,8 +683,8 @@ __global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __
 }
 
 template <typename T, int D, typename OutT>
-hipError_t fwd_typed(const Shape& s, bool causal, const void* q, const void* k, const void* v, void* o, float* lse,
-                     float scale, void* ws, hipStream_t st) {
+hipError_t fwd_typed(const Shape& s, bool causal, const Mask& mask, const float* sinks, const void* q, const void* k,
+                     const void* v, void* o, float* lse, float scale, void* ws, hipStream_t st) {
   const SplitPlan pl = plan(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int n_rb = (int)((G * s.Lq + 31) / 32);
@@ -664,33 +692,39 @@ hipError_t fwd_typed(const Shape& s, bool causal, const void* q, const void* k, 
   float* part_o = (float*)ws;
   float* part_ml = part_o + (int64_t)pl.nsplit * tr * D;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  auto kern = causal ? vec_fwd_kernel<T, D, true, OutT> : vec_fwd_kernel<T, D, false, OutT>;
+  auto kern = causal                     ? vec_fwd_kernel<T, D, true, false, OutT>
+              : mask.kind != kMaskNone ? vec_fwd_kernel<T, D, false, true, OutT>
+                                         : vec_fwd_kernel<T, D, false, false, OutT>;
   hipLaunchKernelGGL(kern, dim3(pl.nsplit * n_rb * s.B * s.Hkv), dim3(64 * vec_waves<D>()), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, part_o, part_ml, (int)s.Hq, G, (int)s.Lq,
-                     (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2);
+                     (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2, mask, sinks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   constexpr int RPB = kThreads / (D / 4);
   hipLaunchKernelGGL((vec_combine_kernel<D, OutT>), dim3((unsigned)((tr + RPB - 1) / RPB)), dim3(kThreads), 0, st,
-                     (const float*)part_o, (const float*)part_ml, (OutT*)o, lse, tr, pl.nsplit);
+                     (const float*)part_o, (const float*)part_ml, (OutT*)o, lse, tr, pl.nsplit, sinks, (int)s.Hq,
+                     (int)s.Lq);
   return hipGetLastError();
 }
 
 template <typename T, int D, typename OutT>
-hipError_t bwd_typed(const Shape& s, bool causal, const void* q, const void* k, const void* v, const void* o,
-                     const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws, float scale, int stages,
-                     hipStream_t st) {
+hipError_t bwd_typed(const Shape& s, bool causal, const Mask& mask, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
+                     float scale, int stages, hipStream_t st) {
   const SplitPlan pl = plan(s);
   const int G = (int)(s.Hq / s.Hkv);
   const int64_t tr = rows_total(s);
   float* dq_part = (float*)ws;
+  float* delta = (float*)((char*)ws + vector_bwd_delta_offset(s));
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   if (stages & kStage0) {
-    auto kern = causal ? vec_bwd_kernel<T, D, true, OutT> : vec_bwd_kernel<T, D, false, OutT>;
+    auto kern = causal                     ? vec_bwd_kernel<T, D, true, false, OutT>
+                : mask.kind != kMaskNone ? vec_bwd_kernel<T, D, false, true, OutT>
+                                           : vec_bwd_kernel<T, D, false, false, OutT>;
     hipLaunchKernelGGL(kern, dim3(pl.nsplit * s.B * s.Hkv), dim3(64 * vec_waves<D>()), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
                        (const uint16_t*)dO, (OutT*)dk, (OutT*)dv, dq_part, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv,
-                       pl.nsplit, (int)pl.split_len, tr, scale_log2, scale);
+                       pl.nsplit, (int)pl.split_len, tr, scale_log2, scale, mask, delta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -711,8 +745,14 @@ size_t vector_fwd_workspace(const Shape& s) {
   return (size_t)pl.nsplit * (size_t)rows_total(s) * (size_t)(s.D + 2) * sizeof(float);
 }
 
+// dQ partials [nsplit][B*Hq*Lq][D], then (256-byte aligned) Delta [B*Hq*Lq].
+size_t vector_bwd_delta_offset(const Shape& s) {
+  const size_t part = (size_t)plan(s).nsplit * (size_t)rows_total(s) * (size_t)s.D * sizeof(float);
+  return (part + 255) / 256 * 256;
+}
+
 size_t vector_bwd_workspace(const Shape& s) {
-  return (size_t)plan(s).nsplit * (size_t)rows_total(s) * (size_t)s.D * sizeof(float);
+  return vector_bwd_delta_offset(s) + (size_t)rows_total(s) * sizeof(float);
 }
 
 #define SDPA_VEC_DISPATCH(FN, ...)                                                                          \
@@ -730,17 +770,18 @@ size_t vector_bwd_workspace(const Shape& s) {
     default: return hipErrorInvalidValue;                                                                   \
   }
 
-hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                             void* o, float* lse, float scale, void* ws, hipStream_t st) {
+hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
+                             const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,
+                             hipStream_t st) {
   if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
-  SDPA_VEC_DISPATCH(fwd_typed, s, causal, q, k, v, o, lse, scale, ws, st)
+  SDPA_VEC_DISPATCH(fwd_typed, s, causal, mask, sinks, q, k, v, o, lse, scale, ws, st)
 }
 
-hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const void* q, const void* k, const void* v,
-                             const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
-                             float scale, int stages, hipStream_t st) {
+hipError_t launch_bwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
+                             const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+                             void* dk, void* dv, void* ws, float scale, int stages, hipStream_t st) {
   if (dt != kBF16 && dt != kF16) return hipErrorInvalidValue;
-  SDPA_VEC_DISPATCH(bwd_typed, s, causal, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
+  SDPA_VEC_DISPATCH(bwd_typed, s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
 }
 
 }  // namespace sdpa

@@ -25,7 +25,8 @@ DTYPES = ("f32", "f16", "bf16")
 
 
 def f32_to_bf16_bits(x):
-    """float32 -> bfloat16 bit patterns (uint16), round to nearest even (finite inputs)."""
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even (finite inputs and
+    infinities; no NaN)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
@@ -98,6 +99,37 @@ def make_case(B, Hq, Hkv, Lq, Lkv, D, dtype, is_causal=False, seed=0, with_grad=
     do = draw((B, Hq, Lq, D)) if with_grad else None
     return Case(B, Hq, Hkv, Lq, Lkv, D, dtype, bool(is_causal),
                 default_scale(D) if scale is None else float(np.float32(scale)), q, k, v, do)
+
+
+def make_mask(kind, shape, dtype, seed=0, p_keep=0.7, empty_rows=0):
+    """A seeded synthetic attention mask of ``shape`` (broadcastable to [B, Hq, Lq, Lkv]).
+
+    kind "bool": each key kept with probability ``p_keep``; every row keeps at least
+    its first key except the first ``empty_rows`` query rows, which keep none.
+    kind "additive": N(0, 4) values in the storage form of ``dtype``, with about 1 in 8
+    entries set to -inf (the first key of each row stays finite unless the row is one
+    of the ``empty_rows``, which are all -inf).
+    Returns a numpy bool array, or a storage array of ``dtype`` (bf16 as bit patterns)."""
+    rng = np.random.default_rng(seed)
+    if kind == "bool":
+        m = rng.random(shape) < p_keep
+        m[..., 0] = True
+        m[..., :empty_rows, :] = False
+        return m
+    if kind == "additive":
+        x = (rng.standard_normal(shape) * 2.0).astype(np.float32)
+        x[rng.random(shape) < 0.125] = -np.inf
+        x[..., 0] = (rng.standard_normal(x[..., 0].shape) * 2.0).astype(np.float32)  # finite
+        x[..., :empty_rows, :] = -np.inf
+        return from_f32(x, dtype)
+    raise ValueError("kind must be 'bool' or 'additive'")
+
+
+def make_sinks(Hq, seed=0, none_heads=()):
+    """Seeded float32 sink logits, N(0, 1) per query head; heads in ``none_heads`` get -inf."""
+    s = np.random.default_rng(seed).standard_normal(Hq).astype(np.float32)
+    s[list(none_heads)] = -np.inf
+    return s
 
 
 def to_torch(arr, dtype, device):

@@ -118,3 +118,40 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.library()
+
+
+def _fwdm(lib, kind=1, mask=1, sb=0, sh=0, sq=16, sinks=0, causal=0, dt=1, mask_addr=None, sinks_addr=None):
+    p = lambda x: ctypes.c_void_p(x * 256 if x else 0)  # noqa: E731  (aligned fake addresses, never dereferenced)
+    m = ctypes.c_void_p(mask_addr) if mask_addr is not None else p(mask)
+    sk = ctypes.c_void_p(sinks_addr) if sinks_addr is not None else p(sinks)
+    return lib.sdpa_fwd_masked(p(1), p(1), p(1), p(1), p(0), 1, 2, 1, 16, 16, 64, 0.125, causal, kind, m, sb, sh, sq,
+                               sk, dt, dt, p(0), 0, None)
+
+
+def _bwdm(lib, kind=1, sinks=0, dsinks=0):
+    p = lambda x: ctypes.c_void_p(x * 256 if x else 0)  # noqa: E731
+    return lib.sdpa_bwd_masked(p(1), p(1), p(1), p(1), p(1), p(1), p(1), p(1), p(1), 1, 2, 1, 16, 16, 64, 0.125, 0,
+                               kind, p(1), 0, 0, 16, p(sinks), p(dsinks), 1, 1, p(1), 1 << 20, None)
+
+
+def test_masked_validation_rejects_before_launch():
+    _no_device()
+    lib = sd.library()
+    assert _fwdm(lib, kind=3) == 7                    # unknown mask kind
+    assert _fwdm(lib, mask=0) == 1                    # mask kind set, no mask
+    assert _fwdm(lib, causal=1) == 3                  # a mask with the causal flag
+    assert _fwdm(lib, sq=-1) == 2                     # negative stride
+    assert _fwdm(lib, sh=1 << 62) == 2                # (Hq-1)*sh beyond int64 / 8
+    assert _fwdm(lib, kind=2, mask_addr=257) == 5     # additive 16-bit mask on an odd address
+    assert _fwdm(lib, kind=1, sinks_addr=258) == 5    # sinks not 4-byte aligned
+    assert _bwdm(lib, sinks=1, dsinks=0) == 1         # sinks without dsinks
+
+
+def test_mask_kind_none_ignores_the_mask_arguments():
+    _no_device()
+    lib = sd.library()
+    # NONE with garbage strides and no pointer validates like sdpa_fwd (here: bad head dim).
+    p = lambda x: ctypes.c_void_p(x * 256 if x else 0)  # noqa: E731
+    st = lib.sdpa_fwd_masked(p(1), p(1), p(1), p(1), p(0), 1, 2, 1, 16, 16, 80, 0.125, 1, 0, p(0), -5, -5, -5, p(0),
+                             1, 1, p(0), 0, None)
+    assert st == 3

@@ -102,3 +102,51 @@ def test_gradcheck_fp32(device):
     q, k, v = (inp.to_torch(getattr(case, n), "f32", device).requires_grad_(True) for n in ("q", "k", "v"))
     fn = lambda a, b, c: sd.attention(a, b, c, scale=case.scale)  # noqa: E731
     assert torch.autograd.gradcheck(fn, (q, k, v), eps=1e-2, atol=2e-3, rtol=2e-2, fast_mode=True)
+
+
+def test_mask_and_sink_rules(monkeypatch):
+    q = torch.empty((1, 4, 8, 64), device="meta")
+    k = torch.empty((1, 2, 16, 64), device="meta")
+    monkeypatch.setattr(torch.Tensor, "device", property(lambda self: torch.device("cuda", 0)))
+    m = torch.empty((1, 1, 8, 16), dtype=torch.bool, device="meta")
+    sd.check_eligible(q, k, k.clone(), False, m, torch.empty(4, device="meta"))
+    with pytest.raises(ValueError, match="not combined"):
+        sd.check_eligible(q, k, k.clone(), True, m)
+    with pytest.raises(ValueError, match="bool or"):
+        sd.check_eligible(q, k, k.clone(), False, torch.empty((8, 16), dtype=torch.float16, device="meta"))
+    with pytest.raises(ValueError, match="broadcast"):
+        sd.check_eligible(q, k, k.clone(), False, torch.empty((1, 3, 8, 16), dtype=torch.bool, device="meta"))
+    with pytest.raises(ValueError, match="no gradient"):
+        sd.check_eligible(q, k, k.clone(), False, torch.empty((8, 16), device="meta", requires_grad=True))
+    with pytest.raises(ValueError, match="sinks"):
+        sd.check_eligible(q, k, k.clone(), False, None, torch.empty(3, device="meta"))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt,Lq", [("bf16", 70), ("f16", 6), ("f32", 20)])
+def test_mask_and_sinks_match_c_abi_bitwise(device, dt, Lq):
+    case = inp.make_case(1, 4, 2, Lq, 90, 64, dt, seed=13)
+    q, k, v, do = (inp.to_torch(getattr(case, n), dt, device) for n in ("q", "k", "v", "do"))
+    mask = torch.from_numpy(inp.make_mask("bool", (1, 1, Lq, 90), dt, seed=1)).to(device)
+    sinks = torch.from_numpy(inp.make_sinks(4, seed=2)).to(device)
+    o_ref, lse_ref = sd.sdpa_fwd(q, k, v, scale=case.scale, attn_mask=mask, sinks=sinks)
+    g_ref = sd.sdpa_bwd(q, k, v, o_ref, lse_ref, do, scale=case.scale, attn_mask=mask, sinks=sinks)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    sa = sinks.clone().requires_grad_(True)
+    o = sd.attention(qa, ka, va, scale=case.scale, attn_mask=mask, sinks=sa)
+    o.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for got, want in zip((qa.grad, ka.grad, va.grad, sa.grad), g_ref):
+        assert torch.equal(got, want)
+
+
+@pytest.mark.gpu
+def test_gradcheck_fp32_with_mask_and_sinks(device):
+    """Backward (dq, dk, dv and dsinks) against finite differences of the masked forward."""
+    case = inp.make_case(1, 2, 1, 6, 9, 32, "f32", seed=7)
+    q, k, v = (inp.to_torch(getattr(case, n), "f32", device).requires_grad_(True) for n in ("q", "k", "v"))
+    mask = torch.from_numpy(inp.make_mask("additive", (1, 2, 6, 9), "f32", seed=3)).to(device)
+    sinks = torch.from_numpy(inp.make_sinks(2, seed=4)).to(device).requires_grad_(True)
+    fn = lambda a, b, c, s: sd.attention(a, b, c, scale=case.scale, attn_mask=mask, sinks=s)  # noqa: E731
+    assert torch.autograd.gradcheck(fn, (q, k, v, sinks), eps=1e-2, atol=2e-3, rtol=2e-2, fast_mode=True)
