@@ -30,7 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 from scaled_dot_product_online_amd import inputs as inp  # noqa: E402
-from scaled_dot_product_online_amd.workloads import BY_NAME, HEADLINE, WORKLOADS, flops  # noqa: E402
+from scaled_dot_product_online_amd.workloads import BY_NAME, HEADLINE, MASKED, WORKLOADS, flops, mask_and_sinks  # noqa: E402
 
 METRIC = "SDPA TFLOP/s fwd & fwd+bwd (bf16/fp16, causal) and % of MFMA peak, 1 GPU"
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense, AMD's published MI355X figures
@@ -68,6 +68,10 @@ class Runner:
         self.case = inp.make_case(B, Hq, Hkv, Lq, Lkv, D, dt, is_causal=causal, seed=0)
         c = self.case
         self.q, self.k, self.v, self.do = (inp.to_torch(getattr(c, n), dt, device) for n in ("q", "k", "v", "do"))
+        mask, sinks = mask_and_sinks(name)
+        self.mask = None if mask is None else torch.from_numpy(mask[1]).to(device)
+        self.sinks = None if sinks is None else torch.from_numpy(sinks).to(device)
+        self.dsinks = None if sinks is None else torch.empty(Hq, dtype=torch.float32, device=device)
         tdt = self.q.dtype
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=device)
@@ -92,12 +96,13 @@ class Runner:
 
     def fwd(self):
         self.sd.sdpa_fwd(self.q, self.k, self.v, scale=self.case.scale, is_causal=self.case.is_causal, out=self.o,
-                         lse=self.lse, workspace=self.ws_f, stream=self.stream)
+                         lse=self.lse, workspace=self.ws_f, stream=self.stream, attn_mask=self.mask,
+                         sinks=self.sinks)
 
     def bwd(self, stage):
         self.sd.sdpa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, scale=self.case.scale,
                          is_causal=self.case.is_causal, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_b,
-                         stream=self.stream, stage=stage)
+                         stream=self.stream, stage=stage, attn_mask=self.mask, sinks=self.sinks, dsinks=self.dsinks)
 
     def timed(self, steps, warmup):
         """Wall time of `steps` steps (synchronised on both sides) and per-kernel event times."""
@@ -191,14 +196,15 @@ def kernel_symbol(runner, label):
     c = runner.case
     t = {"bf16": "bf16_t", "f16": "f16_t", "f32": "float"}[c.dtype]
     causal = "true" if c.is_causal else "false"
+    masked = "true" if runner.mask is not None else "false"
     if runner.path == "tiled":
         base = {"fwd": "fwd_tiled_kernel", "bwd_stage0": "dq_kernel", "bwd_stage1": "dkv_kernel"}[label]
-        return f"{base}<{t}, {c.D}, {causal}, {t}>"
+        return f"{base}<{t}, {c.D}, {causal}, {masked}, {t}>"
     if runner.path == "vector":
         if label == "bwd_stage1":
             return f"vec_dq_reduce_kernel<{c.D}, {t}>"
         base = {"fwd": "vec_fwd_kernel", "bwd_stage0": "vec_bwd_kernel"}[label]
-        return f"{base}<{t}, {c.D}, {causal}, {t}>"
+        return f"{base}<{t}, {c.D}, {causal}, {masked}, {t}>"
     return None
 
 
@@ -230,8 +236,12 @@ def vector_line(device, steps, warmup):
 
 def config_of(name):
     _, B, Hq, Hkv, Lq, Lkv, D, dt, causal = BY_NAME[name]
-    return {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": causal,
-            "scale": "1/sqrt(D)", "inputs": "iid N(0,1), numpy default_rng(0)"}
+    cfg = {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "Lq": Lq, "Lkv": Lkv, "D": D, "causal": causal,
+           "scale": "1/sqrt(D)", "inputs": "iid N(0,1), numpy default_rng(0)"}
+    if name in MASKED:
+        cfg["mask"] = MASKED[name]["mask"]
+        cfg["sinks"] = MASKED[name]["sinks"]
+    return cfg
 
 
 def main():

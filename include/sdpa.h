@@ -208,6 +208,19 @@ sdpa_status_t sdpa_bwd_masked(const void* q, const void* k, const void* v, const
                               sdpa_dtype_t dtype, sdpa_dtype_t out_dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * sdpa_bwd_masked as two stream-ordered stages, as sdpa_bwd_stage is for sdpa_bwd (same
+ * stage contents; dsinks is written by stage 1, from what stage 0 left in the workspace).
+ * `stage` must be 0 or 1 (else SDPA_ERR_VALUE).
+ */
+sdpa_status_t sdpa_bwd_masked_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dO, void* dq, void* dk, void* dv, int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale,
+                                    int is_causal, sdpa_mask_kind_t mask_kind, const void* mask,
+                                    int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q,
+                                    const float* sinks, float* dsinks, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. Never NULL. */
 const char* sdpa_status_str(sdpa_status_t status);
 

@@ -20,7 +20,7 @@ PATH_TILED, PATH_VECTOR, PATH_FP32 = 0, 1, 2
 PATH_NAMES = {PATH_TILED: "tiled", PATH_VECTOR: "vector", PATH_FP32: "fp32"}
 MASK_NONE, MASK_BOOL, MASK_ADDITIVE = 0, 1, 2
 SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_stage", "sdpa_fwd_masked",
-           "sdpa_bwd_masked", "sdpa_status_str")
+           "sdpa_bwd_masked", "sdpa_bwd_masked_stage", "sdpa_status_str")
 
 _lib = None
 
@@ -57,6 +57,8 @@ def library():
     lib.sdpa_fwd_masked.restype = c_int
     lib.sdpa_bwd_masked.argtypes = lib.sdpa_bwd.argtypes[:17] + mask_args + [vp, vp] + lib.sdpa_bwd.argtypes[17:]
     lib.sdpa_bwd_masked.restype = c_int
+    lib.sdpa_bwd_masked_stage.argtypes = [c_int] + lib.sdpa_bwd_masked.argtypes
+    lib.sdpa_bwd_masked_stage.restype = c_int
     lib.sdpa_status_str.argtypes = [c_int]
     lib.sdpa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -195,13 +197,14 @@ def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True
 
 
 def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, stage=None, attn_mask=None, sinks=None):
+             workspace=None, stream=None, stage=None, attn_mask=None, sinks=None, dsinks=None):
     """dQ, dK, dV of sum(O * dO); ``o`` and ``lse`` are what sdpa_fwd returned.
 
-    ``stage`` None runs the whole backward; 0 or 1 runs one stage (sdpa_bwd_stage),
-    in which case the same ``workspace`` must be passed to both stages. With
-    ``attn_mask`` or ``sinks`` (as given to sdpa_fwd) the whole backward runs through
-    sdpa_bwd_masked; with ``sinks`` the result is (dq, dk, dv, dsinks)."""
+    ``stage`` None runs the whole backward; 0 or 1 runs one stage (sdpa_bwd_stage, or
+    sdpa_bwd_masked_stage with a mask or sinks), in which case the same ``workspace``
+    (and, with sinks, ``dsinks``) must be passed to both stages. With ``attn_mask`` or
+    ``sinks`` (as given to sdpa_fwd) the result is (dq, dk, dv, dsinks), dsinks None
+    without sinks."""
     import torch
 
     _contig(q, k, v, o, lse, dO)
@@ -225,11 +228,14 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
         st = library().sdpa_bwd(*head, *tail) if stage is None else library().sdpa_bwd_stage(int(stage), *head, *tail)
         _check(st)
         return dq, dk, dv
-    if stage is not None:
-        raise ValueError("the masked backward runs as one call (no stage argument)")
     kind, m, sb, sh, sq = mask_args(attn_mask, B, Hq, Lq, Lkv, dt)
     sk = _sinks_arg(sinks, Hq)
-    dsinks = torch.empty(Hq, dtype=torch.float32, device=q.device) if sk is not None else None
-    st = library().sdpa_bwd_masked(*head, kind, _ptr(m), sb, sh, sq, _ptr(sk), _ptr(dsinks), *tail)
+    if sk is not None and dsinks is None:
+        dsinks = torch.empty(Hq, dtype=torch.float32, device=q.device)
+    masked = (kind, _ptr(m), sb, sh, sq, _ptr(sk), _ptr(dsinks if sk is not None else None))
+    if stage is None:
+        st = library().sdpa_bwd_masked(*head, *masked, *tail)
+    else:
+        st = library().sdpa_bwd_masked_stage(int(stage), *head, *masked, *tail)
     _check(st)
-    return (dq, dk, dv) if sk is None else (dq, dk, dv, dsinks)
+    return dq, dk, dv, (dsinks if sk is not None else None)

@@ -249,6 +249,19 @@ sdpa_status_t sdpa_bwd_stage(int stage, const void* q, const void* k, const void
                  workspace_bytes, stream);
 }
 
+sdpa_status_t sdpa_bwd_masked_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dO, void* dq, void* dk, void* dv, int64_t B,
+                                    int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D, float scale,
+                                    int is_causal, sdpa_mask_kind_t mask_kind, const void* mask,
+                                    int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q,
+                                    const float* sinks, float* dsinks, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage != 0 && stage != 1) return SDPA_ERR_VALUE;
+  return run_bwd(stage == 0 ? sdpa::kStage0 : sdpa::kStage1, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
+                 scale, is_causal, mask_kind, mask, mask_stride_b, mask_stride_h, mask_stride_q, sinks, dsinks, dtype,
+                 out_dtype, workspace, workspace_bytes, stream);
+}
+
 const char* sdpa_status_str(sdpa_status_t status) {
   switch (status) {
     case SDPA_OK: return "ok";

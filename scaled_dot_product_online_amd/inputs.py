@@ -125,6 +125,12 @@ def make_mask(kind, shape, dtype, seed=0, p_keep=0.7, empty_rows=0):
     raise ValueError("kind must be 'bool' or 'additive'")
 
 
+def make_key_padding_mask(B, Lkv, keep):
+    """Boolean [B, 1, 1, Lkv]: batch b keeps its first keep[b] keys (a padded batch)."""
+    keep = np.asarray(keep).reshape(B, 1, 1, 1)
+    return np.arange(Lkv)[None, None, None, :] < keep
+
+
 def make_sinks(Hq, seed=0, none_heads=()):
     """Seeded float32 sink logits, N(0, 1) per query head; heads in ``none_heads`` get -inf."""
     s = np.random.default_rng(seed).standard_normal(Hq).astype(np.float32)

@@ -19,6 +19,12 @@ Each entry is (name, B, Hq, Hkv, Lq, Lkv, D, dtype, is_causal). Sources:
 * ``*_d96`` and ``*_d256`` — the GQA and short-query shapes above at head dims 96
   (listed in the same pull request's "Test Plan") and 256 (which that pull request's
   vector VJP leaves out for lack of threadgroup memory, "Limitations").
+* ``*_keypad*`` and ``*_sinks*`` — the GQA and short-query shapes with a boolean
+  key-padding mask (batch b keeps its first Lkv - (b mod 4)*Lkv/8 keys) and/or one sink logit
+  per query head (N(0, 1)): the masks and sinks that mps-flash-sdpa ("When MFA
+  Dispatches vs. Falls Back") and the MLX pull request ("Limitations") hand back to
+  unfused attention. Their work is counted like the unmasked shape's (the kernels
+  visit every key tile; a mask removes no tile).
 """
 
 from __future__ import annotations
@@ -43,7 +49,33 @@ WORKLOADS += [
     ("bf16_gqa8_causal_4k_d256", 4, 32, 4, 4096, 4096, 256, "bf16", True),
     ("vec_bf16_lq8_d96", 16, 32, 8, 8, 8192, 96, "bf16", False),
     ("vec_bf16_lq8_d256", 16, 32, 8, 8, 8192, 256, "bf16", False),
+    ("bf16_gqa8_keypad_4k_d128", 4, 32, 4, 4096, 4096, 128, "bf16", False),
+    ("bf16_gqa8_causal_sinks_4k_d128", 4, 32, 4, 4096, 4096, 128, "bf16", True),
+    ("vec_bf16_lq8_d128_keypad_sinks", 16, 32, 8, 8, 8192, 128, "bf16", False),
 ]
+
+# Masks and sinks of the workloads that have them: "keypad" = inputs.make_key_padding_mask
+# with keep[b] = Lkv - (b % 4) * Lkv // 8; sinks = inputs.make_sinks(Hq, seed=0).
+MASKED = {
+    "bf16_gqa8_keypad_4k_d128": {"mask": "keypad", "sinks": False},
+    "bf16_gqa8_causal_sinks_4k_d128": {"mask": None, "sinks": True},
+    "vec_bf16_lq8_d128_keypad_sinks": {"mask": "keypad", "sinks": True},
+}
+
+
+def mask_and_sinks(name):
+    """(mask, sinks) for a workload: mask None or ("bool", array), sinks None or float32 [Hq]."""
+    from . import inputs as inp
+
+    spec = MASKED.get(name)
+    if spec is None:
+        return None, None
+    _, B, Hq, Hkv, Lq, Lkv, D, dt, causal = BY_NAME[name]
+    mask = None
+    if spec["mask"] == "keypad":
+        mask = ("bool", inp.make_key_padding_mask(B, Lkv, [Lkv - (b % 4) * Lkv // 8 for b in range(B)]))
+    sinks = inp.make_sinks(Hq, seed=0) if spec["sinks"] else None
+    return mask, sinks
 
 BY_NAME = {w[0]: w for w in WORKLOADS}
 

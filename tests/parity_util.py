@@ -166,30 +166,43 @@ def compare(case, got, want, backward=True):
     return report
 
 
-def reference_group(case, out_dtype, b, hk, backward=True):
+def _group_mask(m, b, hs):
+    """Batch b and query heads hs of a mask broadcastable to [B, Hq, Lq, Lkv] (size-1 axes kept)."""
+    if m is None:
+        return None
+    m = m.reshape((1,) * (4 - m.ndim) + m.shape)
+    return m[(slice(b, b + 1) if m.shape[0] > 1 else slice(0, 1)), (hs if m.shape[1] > 1 else slice(0, 1))]
+
+
+def reference_group(case, out_dtype, b, hk, backward=True, mask=None, sinks=None):
     """Oracle and model values for the G query heads of KV group (b, hk) only.
 
     Used at full workload sizes, where the whole-tensor oracle would take minutes.
     Returns arrays shaped like the group's slices: o/lse/dq [G, Lq, ...], dk/dv [Lkv, D].
+    (dsinks sums over every batch, so a group cannot check it.)
     """
     G = case.Hq // case.Hkv
     hs = slice(hk * G, (hk + 1) * G)
     q = inp.as_float64(case.q[b:b + 1, hs], case.dtype)
     k = inp.as_float64(case.k[b:b + 1, hk:hk + 1], case.dtype)
     v = inp.as_float64(case.v[b:b + 1, hk:hk + 1], case.dtype)
-    o, lse = ref.attention_forward(q, k, v, case.scale, case.is_causal)
+    m = _group_mask(oracle_mask(case, mask), b, hs)
+    sk = None if sinks is None else np.asarray(sinks, dtype=np.float64)[hs]
+    o, lse = ref.attention_forward(q, k, v, case.scale, case.is_causal, mask=m, sinks=sk)
     op = case.dtype
     pn = path_name(case)
-    o_model = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, out_dtype, KV_BLOCK[pn], slack=SLACK[pn])
-    o_pre = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, "f64", KV_BLOCK[pn], slack=SLACK[pn])
+    o_model = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, out_dtype, KV_BLOCK[pn], slack=SLACK[pn],
+                                 mask=m, sinks=sk)
+    o_pre = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, "f64", KV_BLOCK[pn], slack=SLACK[pn],
+                               mask=m, sinks=sk)
     out = {"o": o[0], "lse": lse[0], "o_model": o_pre[0], "out_dtype": out_dtype}
     if backward:
         do = inp.as_float64(case.do[b:b + 1, hs], case.dtype)
-        dq, dk, dv = ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0)
+        dq, dk, dv = ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0, mask=m, sinks=sk)
         mdq, mdk, mdv = rf.emulate_backward_group(q, k, v, do, o_model, lse, case.scale, case.is_causal, op,
-                                                  "f64", 0, 0)
+                                                  "f64", 0, 0, mask=m)
         alt = rf.emulate_backward_group(q, k, v, do, rf.round_to(o, out_dtype), lse, case.scale, case.is_causal, op,
-                                        "f64", 0, 0)
+                                        "f64", 0, 0, mask=m)
         out.update(dq=dq, dk=dk, dv=dv, dq_model=mdq, dk_model=mdk, dv_model=mdv,
                    **{n + "_spread": float(np.abs(a - b).max()) for n, a, b in zip(("dq", "dk", "dv"), (mdq, mdk, mdv),
                                                                                     alt)})
