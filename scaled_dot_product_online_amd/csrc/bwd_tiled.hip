@@ -200,14 +200,27 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           float ds[8];
+          // The mask's bias of keys kt0 + kb*32 + 8*(2*c2 + h) + 4g + 0..3 (element e = 4h + j).
+          float bias[8];
+          if constexpr (HAS_MASK) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int key0 = kt0 + kb * 32 + 8 * (2 * c2 + h) + 4 * g;
+              if (mask.vec4 && key0 < Lkv) {
+                mask_bias4_log2<T>(mask.p, mask.kind, mrow + key0, bias + 4 * h);
+              } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  bias[4 * h + j] =
+                      key0 + j < Lkv ? mask_bias_log2<T>(mask.p, mask.kind, mrow + key0 + j) : -INFINITY;
+              }
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int i = 8 * c2 + e;
             float nb = -lse2;
-            if constexpr (HAS_MASK) {  // the mask's bias of key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g
-              const int key = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) + 4 * g;
-              nb = (key < Lkv ? mask_bias_log2<T>(mask.p, mask.kind, mrow + key) : -INFINITY) - lse2;
-            }
+            if constexpr (HAS_MASK) nb = bias[e] - lse2;
             float p = fast_exp2(fminf(fmaf(s[i], scale_log2, nb), 0.f));
             if constexpr (EDGE)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
               p = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) < klim ? p : 0.f;
@@ -397,6 +410,11 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
       }
     };
 
+    // A mask that does not vary along queries (stride 0: key padding) has one bias per
+    // lane and tile.
+    float kbias = 0.f;
+    if constexpr (HAS_MASK)
+      if (mask.sq == 0) kbias = mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh);
     // Row statistics of this lane's queries qm*16 + 4*q4 + j.
     f32x4_t sa[4], sb[4];
 #pragma unroll
@@ -449,8 +467,12 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
           for (int j = 0; j < 4; ++j) {
             float nb = -l2[j];
             if constexpr (HAS_MASK) {  // bias of (query t0 + qm*16 + 4*q4 + j, key krow)
-              const int qi = min(t0 + qm * 16 + 4 * q4 + j, Lq - 1);
-              nb += mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh + (int64_t)qi * mask.sq);
+              if (mask.sq == 0) {
+                nb += kbias;
+              } else {
+                const int qi = min(t0 + qm * 16 + 4 * q4 + j, Lq - 1);
+                nb += mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh + (int64_t)qi * mask.sq);
+              }
             }
             float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, nb), 0.f));
             if constexpr (EDGE) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, sees key krow

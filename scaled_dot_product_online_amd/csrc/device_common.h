@@ -287,6 +287,22 @@ __device__ __forceinline__ float mask_bias_log2(const void* p, int kind, int64_t
   else
     return to_f32<T>(((const uint16_t*)p)[off]) * kLog2e;
 }
+// The same for the 4 consecutive keys at element offset `off`, with one aligned load
+// (off a multiple of 4, and the mask's vec4 property). 16-bit operand types only.
+template <typename T>
+__device__ __forceinline__ void mask_bias4_log2(const void* p, int kind, int64_t off, float* b) {
+  if (kind == 1) {
+    const uint32_t w = *(const uint32_t*)((const uint8_t*)p + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = ((w >> (8 * j)) & 0xffu) ? 0.f : -INFINITY;
+  } else {
+    const u32x2_t w = *(const u32x2_t*)((const uint16_t*)p + off);
+    b[0] = lo_f32<T>(w[0]) * kLog2e;
+    b[1] = hi_f32<T>(w[0]) * kLog2e;
+    b[2] = lo_f32<T>(w[1]) * kLog2e;
+    b[3] = hi_f32<T>(w[1]) * kLog2e;
+  }
+}
 __device__ __forceinline__ float load_f32(const bf16_t* p) { return to_f32<bf16_t>(p->bits); }
 __device__ __forceinline__ float load_f32(const f16_t* p) { return to_f32<f16_t>(p->bits); }
 

@@ -147,10 +147,19 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
 #pragma unroll
       for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          s[kb][i] = key < Lkv ? fmaf(s[kb][i], scale_log2, mask_bias_log2<T>(mask.p, mask.kind, mrow + key))
-                               : -INFINITY;
+        for (int i4 = 0; i4 < 4; ++i4) {  // keys key0 .. key0 + 3
+          const int key0 = kt0 + kb * 32 + 8 * i4 + 4 * g;
+          float bias[4];
+          if (mask.vec4 && key0 < Lkv) {
+            mask_bias4_log2<T>(mask.p, mask.kind, mrow + key0, bias);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              bias[j] = key0 + j < Lkv ? mask_bias_log2<T>(mask.p, mask.kind, mrow + key0 + j) : -INFINITY;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            s[kb][4 * i4 + j] = key0 + j < Lkv ? fmaf(s[kb][4 * i4 + j], scale_log2, bias[j]) : -INFINITY;
         }
     } else if ((kt0 + kFwdBN > Lkv) || (CAUSAL && kt0 + kFwdBN - 1 > q0 + co)) {
       // Mask (only tiles that reach past the diagonal or the end), then the row max on raw scores.

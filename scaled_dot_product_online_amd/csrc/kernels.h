@@ -20,14 +20,17 @@ enum { kStage0 = 1, kStage1 = 2, kStagesAll = 3 };
 // Attention mask as the kernels read it (validated by the caller). Element (b, h, i, j)
 // sits at p + b*sb + h*sh + i*sq + j elements; a stride of 0 broadcasts. kind: boolean
 // bytes (nonzero keeps the key) or additive values in the operand type. A mask is never
-// combined with causal masking.
+// combined with causal masking. vec4: the base and every stride are multiples of 4
+// elements (16 bytes for float32 masks) and Lkv is a multiple of 4, so 4 consecutive keys
+// from a key index that is a multiple of 4 are one aligned load.
 enum { kMaskNone = 0, kMaskBool = 1, kMaskAdd = 2 };
 struct Mask {
   const void* p;
   int kind;
+  int vec4;
   int64_t sb, sh, sq;
 };
-constexpr Mask kNoMask = {nullptr, kMaskNone, 0, 0, 0};
+constexpr Mask kNoMask = {nullptr, kMaskNone, 0, 0, 0, 0};
 
 // dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * Delta(b,h,i), with Delta(b,h,i) at
 // delta[((b*Hq + h) * pitch + i) * es] (delta.hip). One deterministic reduction per head.

@@ -85,7 +85,8 @@ sdpa_status_t check_mask(int kind, const void* mask, int64_t sb, int64_t sh, int
     return SDPA_ERR_SHAPE;
   const uintptr_t esz = kind == SDPA_MASK_BOOL ? 1 : (dtype == SDPA_F32 ? 4 : 2);
   if (((uintptr_t)mask & (esz - 1)) != 0) return SDPA_ERR_ALIGN;
-  *m = sdpa::Mask{mask, kind == SDPA_MASK_BOOL ? sdpa::kMaskBool : sdpa::kMaskAdd, sb, sh, sq};
+  const bool vec4 = ((uintptr_t)mask % (4 * esz)) == 0 && sb % 4 == 0 && sh % 4 == 0 && sq % 4 == 0 && Lkv % 4 == 0;
+  *m = sdpa::Mask{mask, kind == SDPA_MASK_BOOL ? sdpa::kMaskBool : sdpa::kMaskAdd, vec4 ? 1 : 0, sb, sh, sq};
   return SDPA_OK;
 }
 

@@ -185,15 +185,27 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
         if (key >= kb1 || (CAUSAL && key > qlim)) s[i] = -INFINITY;
       }
     }
+    float bias[16];
+    if constexpr (HAS_MASK) {  // keys t0 + 8*i4 + 4g + 0..3 (past the end: clamped, and already -inf)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int key0 = t0 + 8 * i4 + 4 * g;
+        if (mask.vec4 && key0 < Lkv) {
+          mask_bias4_log2<T>(mask.p, mask.kind, mrow + key0, bias + 4 * i4);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            bias[4 * i4 + j] = mask_bias_log2<T>(mask.p, mask.kind, mrow + min(key0 + j, Lkv - 1));
+        }
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (HAS_MASK) {  // scale and the mask's bias, keys past the segment stay -inf
-        const int key = min(t0 + 8 * (i >> 2) + 4 * g + (i & 3), Lkv - 1);
-        s[i] = fmaf(s[i], scale_log2, mask_bias_log2<T>(mask.p, mask.kind, mrow + key));
-      } else {
+      if constexpr (HAS_MASK)  // scale and the mask's bias, keys past the segment stay -inf
+        s[i] = fmaf(s[i], scale_log2, bias[i]);
+      else
         s[i] *= scale_log2;
-      }
       tmax = fmaxf(tmax, s[i]);
     }
     tmax = half_swap_max(tmax);
@@ -481,6 +493,11 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
     uint16_t* dsw = kTight ? (uint16_t*)const_cast<uint8_t*>(vt) : ds_lds[wave];  // V is consumed once dP is formed
     const int t0 = kb0 + st * kVecKeys;
     const int key = t0 + n;  // this lane's key column
+    // A mask that varies only along keys (query and head strides 0) has one bias per lane.
+    float kbias = 0.f;
+    if constexpr (HAS_MASK)
+      if (mask.sq == 0 && mask.sh == 0)
+        kbias = mask_bias_log2<T>(mask.p, mask.kind, (int64_t)b * mask.sb + min(key, Lkv - 1));
     // S = Q K^T and dP = dO V^T: rows = packed query rows, columns = this wave's 32 keys.
     f32x16_t s, dp;
 #pragma unroll
@@ -516,10 +533,14 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
           const int i = 8 * c2 + 4 * h + j;
           float nb = -l4[j];
           if constexpr (HAS_MASK) {  // bias of (packed row r0 + j, key), both clamped into range
-            const int r = min(r0 + j, rows - 1);
-            nb += mask_bias_log2<T>(mask.p, mask.kind,
-                                    (int64_t)b * mask.sb + (int64_t)(hk * G + r / Lq) * mask.sh +
-                                        (int64_t)(r % Lq) * mask.sq + min(key, Lkv - 1));
+            if (mask.sq == 0 && mask.sh == 0) {
+              nb += kbias;
+            } else {
+              const int r = min(r0 + j, rows - 1);
+              nb += mask_bias_log2<T>(mask.p, mask.kind,
+                                      (int64_t)b * mask.sb + (int64_t)(hk * G + r / Lq) * mask.sh +
+                                          (int64_t)(r % Lq) * mask.sq + min(key, Lkv - 1));
+            }
           }
           float p = fast_exp2(fminf(fmaf(s[i], scale_log2, nb), 0.f));
           if (r0 + j >= rows || key >= kb1 || (CAUSAL && key > lim4[j])) p = 0.f;
