@@ -201,6 +201,15 @@ __device__ __forceinline__ void wave_sync() {
 __device__ __forceinline__ void settle(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 // Scheduling fence: the compiler moves no instruction across it.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Compensated addition, sum += x, carrying each addition's rounding error in c (Kahan's
+// summation, 1965): the error of a running sum stays a few ulps however many similar
+// terms are added. Both sum and c are rescaled together when the sum is.
+__device__ __forceinline__ void kahan_add(float& sum, float& c, float x) {
+  const float y = x - c;
+  const float t = sum + y;
+  c = (t - sum) - y;
+  sum = t;
+}
 // Wave index as a scalar (lets the compiler keep per-wave quantities uniform).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 

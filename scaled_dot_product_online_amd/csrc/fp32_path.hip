@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     qv[e] = (qrow < Lq) ? q[((int64_t)bh * Lq + qrow) * D + slice * TL::W + e] : 0.f;
     acc[e] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, lc = 0.f;  // row max, row sum and its compensation
   if (sinks != nullptr && sinks[hq] > -INFINITY) {  // the sink: a first key with no value
     m = sinks[hq] * kLog2e;
     l = 1.f;
@@ -104,16 +104,19 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(const float* __res
     const float alpha = fast_exp2(m - m_use);
     m = m_new;
     l *= alpha;
+    lc *= alpha;
 #pragma unroll
     for (int e = 0; e < TL::W; ++e) acc[e] *= alpha;
+    float tsum = 0.f;  // the tile's probabilities, added to the row sum once
 #pragma unroll
     for (int j = 0; j < kF32BN; ++j) {
       const float p = fast_exp2(s[j] - m_use);
-      l += p;
+      tsum += p;
       const float* vr = v_lds + j * TL::PITCH + slice * TL::SP;
 #pragma unroll
       for (int e = 0; e < TL::W; ++e) acc[e] = fmaf(p, vr[e], acc[e]);
     }
+    kahan_add(l, lc, tsum);
   }
   if (qrow < Lq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;

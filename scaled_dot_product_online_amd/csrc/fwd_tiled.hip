@@ -83,6 +83,7 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m = -INFINITY;  // reference row max of the log2-domain scores (see kRescaleSlack)
   float lsum = 0.f;     // this lane's share of the running row sum
+  float lcomp = 0.f;    // its compensation term (kahan_add)
   if (sinks != nullptr) {  // the sink: a first "key" of score sink*log2e and no value
     const float sk = sinks[hq] * kLog2e;
     if (sk > -INFINITY) {
@@ -186,6 +187,7 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
       const float alpha = (MASKED && !grow) ? 1.f : fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
+      lcomp *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -195,6 +197,10 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
 
     // P = 2^(s*scale*log2e - m), rounded to the operand type, then O^T += V^T P^T.
     // B operand chunk (kb, c2) covers keys kb*32 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}.
+    // The tile's probabilities are summed first and added to the row sum once, with
+    // compensation: added one by one, over millions of keys each term falls near the
+    // sum's rounding step.
+    float tsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(fmaf(s[kb][8 * c2 + e], sl2, neg_m));
-          lsum += p[e];
+          tsum += p[e];
         }
         const u32x4_t pop = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]),
                                       pack2<T>(p[6], p[7])};
@@ -216,6 +222,7 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
           oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop, oacc[db]);
         }
       }
+    kahan_add(lsum, lcomp, tsum);
   }
 
   const float l = half_swap_sum(lsum);

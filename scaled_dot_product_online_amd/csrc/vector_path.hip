@@ -149,7 +149,7 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = -INFINITY, lsum = 0.f;
+  float m = -INFINITY, lsum = 0.f, lcomp = 0.f;  // row max, row sum and its compensation
 
   for (int st = 0; st < 2 && st < steps; ++st) {
     fill_k(st);
@@ -214,21 +214,24 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
     const float alpha = fast_exp2(m - m_use);
     m = m_new;
     lsum *= alpha;
+    lcomp *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     u32x4_t pop[2];
+    float tsum = 0.f;  // the step's probabilities, added to the row sum once
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = fast_exp2(s[8 * c2 + e] - m_use);
-        lsum += p[e];
+        tsum += p[e];
       }
       pop[c2] = (u32x4_t){pack2<T>(p[0], p[1]), pack2<T>(p[2], p[3]), pack2<T>(p[4], p[5]), pack2<T>(p[6], p[7])};
     }
+    kahan_add(lsum, lcomp, tsum);
     // O^T += V^T P^T; B operand chunk c2 covers keys t0 + 16*c2 + {4g..4g+3, 8+4g..8+4g+3}.
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
