@@ -13,6 +13,8 @@ and the block problem is checked against the oracle with the usual bound
 (tests/parity_util.py). Every copy's dK / dV must also be bit-identical to the
 first copy's (a key's gradients depend only on its own row and the query rows).
 Both kernel families run: the short-query path (Lq = 4) and the tiled path (Lq = 16).
+The last test takes the query side to the same length (Q and dO repeated), where the
+dK / dV accumulations run over all 8.4M queries.
 """
 
 import math
@@ -54,3 +56,31 @@ def test_repeated_keys_at_max_length(device, Lq):
     rep = compare(case, got, reference(case, "f32"))
     print(" ".join(f"{n}={e:.2e}/{b:.2e}" for n, (e, b, _) in rep.items()), flush=True)
     assert np.all(np.isfinite(got["lse"]))
+
+
+def test_repeated_queries_at_max_length(device):
+    """The other side of the limit: Lq = R * 4096 queries (Q and dO are R copies of one
+    block) against one 4096-key block. Every copy's O, LSE and dQ equal the block's, and
+    dK, dV (accumulated over all 8.4M queries) are R times the block's."""
+    import torch
+
+    import scaled_dot_product_online_amd as sd
+
+    case = inp.make_case(1, 2, 1, BLOCK, BLOCK, D, "bf16", seed=4)
+    qb, k, v, dob = (inp.to_torch(getattr(case, n), "bf16", device) for n in ("q", "k", "v", "do"))
+    q = qb.repeat(1, 1, R, 1).contiguous()
+    do = dob.repeat(1, 1, R, 1).contiguous()
+    print(f"[max-size] Lq={q.shape[2]} Lkv={BLOCK}", flush=True)
+    o, lse = sd.sdpa_fwd(q, k, v, scale=case.scale, out_dtype=torch.float32)
+    dq, dk, dv = sd.sdpa_bwd(q, k, v, o, lse, do, scale=case.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del q, do
+    o_r, l_r, dq_r = (t.view(1, 2, R, BLOCK, *t.shape[3:]) for t in (o, lse, dq))
+    for t in (o_r, l_r, dq_r):  # every query copy computes the same rows
+        assert bool((t == t[:, :, :1]).all()), "query copies differ"
+    got = {"o": inp.from_torch(o_r[:, :, 0], "f32"), "lse": inp.from_torch(l_r[:, :, 0], "f32"),
+           "dq": inp.from_torch(dq_r[:, :, 0], "f32"), "dk": inp.from_torch(dk, "f32") / R,
+           "dv": inp.from_torch(dv, "f32") / R}
+    del o, lse, dq, o_r, l_r, dq_r
+    rep = compare(case, got, reference(case, "f32"))
+    print(" ".join(f"{n}={e:.2e}/{b:.2e}" for n, (e, b, _) in rep.items()), flush=True)
