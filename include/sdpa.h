@@ -38,7 +38,9 @@
  *             16-byte aligned. Outputs must not alias inputs or each other.
  *             The library never allocates, frees, retains a pointer after the
  *             call returns, or synchronises; work is enqueued on `stream`
- *             (a hipStream_t; NULL means the default stream).
+ *             (a hipStream_t; NULL means the default stream). It enqueues kernel
+ *             launches only (no memory sets or copies), so the calls can be
+ *             captured in a HIP graph and replayed.
  * Workspace   Caller-owned device scratch of at least sdpa_workspace_bytes(...)
  *             bytes (may be NULL when that is 0), 256-byte aligned. Its contents
  *             on entry do not matter. Calls that share a workspace must be
