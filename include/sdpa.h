@@ -97,7 +97,11 @@ int sdpa_select_path(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D
 /*
  * Bytes of workspace sdpa_fwd (backward = 0) or sdpa_bwd (backward = 1) needs
  * for these sizes; 0 if none. Pure host function. Returns (size_t)-1 when the
- * sizes are invalid.
+ * sizes are invalid. The forward needs one on the short-query path, and on the
+ * tiled path when its grid of (128-query block, head) pairs is too small to give
+ * every compute unit two workgroups: there the keys are split over several
+ * workgroups whose fp32 partials (unnormalised O, running max, row sum) the
+ * workspace holds until a second kernel merges them.
  */
 size_t sdpa_workspace_bytes(int backward, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
                             int64_t D, int is_causal, sdpa_dtype_t dtype);

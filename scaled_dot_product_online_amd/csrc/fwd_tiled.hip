@@ -22,6 +22,12 @@
 // already sit in the B-operand layout of O^T += V^T P^T. V^T is read from the
 // row-major V tile with the LDS transpose read.
 //
+// Small grids: when there are fewer (query block, head) workgroups than two per CU (one
+// head of a few thousand queries, say), the keys are split into contiguous ranges of whole
+// tiles handled by separate workgroups. Each writes its rows' unnormalised O, reference
+// maximum m and row sum l (fp32), and a combine kernel merges the splits exactly as the
+// online softmax merges tiles: m* = max m_s, O = sum O_s 2^(m_s - m*) / sum l_s 2^(m_s - m*).
+//
 // Masks and sinks (MASKED instantiations; the sink is a runtime pointer): the mask's
 // bias enters every score in the log2 domain before the row maximum, and a row's sink
 // logit seeds the reference maximum and the row sum as if it were a first key with no
@@ -46,18 +52,21 @@ template <typename T, int D, bool CAUSAL, bool MASKED, typename OutT>
 __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     OutT* __restrict__ o, float* __restrict__ lse, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
-    float scale_log2, Mask mask, const float* __restrict__ sinks) {
+    float scale_log2, Mask mask, const float* __restrict__ sinks, int nsplit, int split_tiles,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
   using TL = SwzTile<D>;
   constexpr int kFwdBN = fwd_bn<D>();
   constexpr int TILE = kFwdBN * TL::RB;  // bytes of one K or V tile
   // [buffer][K, V] tiles; buffer t & 1 holds key tile t while tile t + 1 streams into the other.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
 
-  // Work id: query block major (longest causal rows first), then (b, hq) with the
-  // G heads of a KV group adjacent and co-located on one XCD.
-  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh, G);
-  int qblk = wid / n_bh;
-  const int bh = wid - qblk * n_bh;
+  // Work id: query block major (longest causal rows first), then key split, then (b, hq)
+  // with the G heads of a KV group adjacent and co-located on one XCD.
+  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh * nsplit, G);
+  int qblk = wid / (n_bh * nsplit);
+  const int rest = wid - qblk * (n_bh * nsplit);
+  const int split = rest / n_bh;
+  const int bh = rest - split * n_bh;
   if (CAUSAL) qblk = n_qblk - 1 - qblk;
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hk = hq / G, Hkv = Hq / G;
@@ -101,6 +110,9 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
   const int co = Lkv - Lq;
   const int kv_end = CAUSAL ? min(Lkv, qblk * kFwdBM + kFwdBM + co) : Lkv;
   const int ntiles = (kv_end + kFwdBN - 1) / kFwdBN;
+  // This workgroup's key tiles: all of them, or one split's range (empty for a causal block
+  // that ends before the split begins).
+  const int t_lo = split * split_tiles, t_hi = min(ntiles, t_lo + split_tiles);
   const int key_lim = CAUSAL ? min(Lkv, qrow + 1 + co) : Lkv;  // keys >= key_lim are masked for this row
 
   // Per-lane LDS offsets. K rows (16-byte reads): row kb*32 + n, chunk 2c + g.
@@ -114,12 +126,15 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
 
   const srd_t rk = make_srd(k + kvoff, (uint32_t)Lkv * D * 2);
   const srd_t rv = make_srd(v + kvoff, (uint32_t)Lkv * D * 2);
-  TL::template dma_fill<kFwdBN>(rk, lds, 0, wave, 4, lane);
-  TL::template dma_fill<kFwdBN>(rv, lds + TILE, 0, wave, 4, lane);
-  for (int t = 0; t < ntiles; ++t) {
+  if (t_lo < t_hi) {
+    uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
+    TL::template dma_fill<kFwdBN>(rk, b0, t_lo * kFwdBN, wave, 4, lane);
+    TL::template dma_fill<kFwdBN>(rv, b0 + TILE, t_lo * kFwdBN, wave, 4, lane);
+  }
+  for (int t = t_lo; t < t_hi; ++t) {
     wait_vmem();
     __syncthreads();  // tile t is in LDS; every wave has finished tile t - 1
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_hi) {
       uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
       TL::template dma_fill<kFwdBN>(rk, nb, (t + 1) * kFwdBN, wave, 4, lane);
       TL::template dma_fill<kFwdBN>(rv, nb + TILE, (t + 1) * kFwdBN, wave, 4, lane);
@@ -182,9 +197,9 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     const bool grow = tmax > m + kRescaleSlack;
     if (__any(grow)) {
       const float m_new = grow ? tmax : m;
-      // A row that did not move keeps its scale (with a mask its m may still be -inf,
-      // where m - m_new would be NaN).
-      const float alpha = (MASKED && !grow) ? 1.f : fast_exp2(m - m_new);
+      // A row that did not move keeps its scale: its m may still be -inf (a mask, or a key
+      // split that starts past the row's causal limit), where m - m_new would be NaN.
+      const float alpha = grow ? fast_exp2(m - m_new) : 1.f;
       m = m_new;
       lsum *= alpha;
       lcomp *= alpha;
@@ -226,6 +241,20 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
   }
 
   const float l = half_swap_sum(lsum);
+  if (part_o != nullptr) {  // one key split: unnormalised partials [split][b*Hq*Lq + hq*Lq + q]
+    if (qrow < Lq) {
+      const int64_t prow = ((int64_t)split * n_bh + bh) * Lq + qrow;
+      float* po = part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4_t*)(po + db * 32 + 8 * r4 + 4 * g) =
+              (f32x4_t){oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]};
+      if (g == 0) *(f32x2_t*)(part_ml + prow * 2) = (f32x2_t){m, l};
+    }
+    return;
+  }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (qrow < Lq) {
     OutT* orow = o + ((int64_t)bh * Lq + qrow) * D;
@@ -240,49 +269,80 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
 }
 
 template <typename T, int D, bool C, bool M, typename OutT>
-hipError_t launch_typed(const Shape& s, const Mask& mask, const float* sinks, const void* q, const void* k,
-                        const void* v, void* o, float* lse, float scale, hipStream_t st) {
+hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const float* sinks, const void* q, const void* k,
+                        const void* v, void* o, float* lse, float scale, void* ws, hipStream_t st) {
   const int n_qblk = (int)((s.Lq + kFwdBM - 1) / kFwdBM);
   const int n_bh = (int)(s.B * s.Hq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh), dim3(kFwdThreads), 0, st,
+  constexpr int BN = fwd_bn<D>();
+  const int nt = (int)((s.Lkv + BN - 1) / BN);
+  const int nsplit = tiled_fwd_splits(s);
+  const int split_tiles = (nt + nsplit - 1) / nsplit;
+  float* part_o = nsplit > 1 ? (float*)ws : nullptr;
+  float* part_ml = nsplit > 1 ? part_o + (int64_t)nsplit * s.B * s.Hq * s.Lq * s.D : nullptr;
+  // With key splits the sink joins in the combine kernel, once per row.
+  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kFwdThreads), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, (int)s.Hq,
-                     (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, mask, sinks);
-  return hipGetLastError();
+                     (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, mask,
+                     nsplit > 1 ? nullptr : sinks, nsplit, split_tiles, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  return launch_split_combine(s, out, nsplit, part_o, part_ml, sinks, o, lse, st);
 }
 
 template <typename T, int D, typename OutT>
-hipError_t launch_mode(const Shape& s, bool causal, const Mask& mask, const float* sinks, const void* q,
-                       const void* k, const void* v, void* o, float* lse, float scale, hipStream_t st) {
-  if (causal) return launch_typed<T, D, true, false, OutT>(s, mask, sinks, q, k, v, o, lse, scale, st);
-  if (mask.kind != kMaskNone) return launch_typed<T, D, false, true, OutT>(s, mask, sinks, q, k, v, o, lse, scale, st);
-  return launch_typed<T, D, false, false, OutT>(s, mask, sinks, q, k, v, o, lse, scale, st);
+hipError_t launch_mode(const Shape& s, Dt out, bool causal, const Mask& mask, const float* sinks, const void* q,
+                       const void* k, const void* v, void* o, float* lse, float scale, void* ws, hipStream_t st) {
+  if (causal) return launch_typed<T, D, true, false, OutT>(s, out, mask, sinks, q, k, v, o, lse, scale, ws, st);
+  if (mask.kind != kMaskNone)
+    return launch_typed<T, D, false, true, OutT>(s, out, mask, sinks, q, k, v, o, lse, scale, ws, st);
+  return launch_typed<T, D, false, false, OutT>(s, out, mask, sinks, q, k, v, o, lse, scale, ws, st);
 }
 
 template <typename T, typename OutT>
-hipError_t launch_d(const Shape& s, bool causal, const Mask& mask, const float* sinks, const void* q, const void* k,
-                    const void* v, void* o, float* lse, float scale, hipStream_t st) {
+hipError_t launch_d(const Shape& s, Dt out, bool causal, const Mask& mask, const float* sinks, const void* q,
+                    const void* k, const void* v, void* o, float* lse, float scale, void* ws, hipStream_t st) {
   switch (s.D) {
-    case 32: return launch_mode<T, 32, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
-    case 64: return launch_mode<T, 64, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
-    case 96: return launch_mode<T, 96, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
-    case 128: return launch_mode<T, 128, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
-    case 256: return launch_mode<T, 256, OutT>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    case 32: return launch_mode<T, 32, OutT>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
+    case 64: return launch_mode<T, 64, OutT>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
+    case 96: return launch_mode<T, 96, OutT>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
+    case 128: return launch_mode<T, 128, OutT>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
+    case 256: return launch_mode<T, 256, OutT>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+// Key splits: enough workgroups for two per CU (256 CUs), each split keeping at least 4 key
+// tiles on average, at most 16 splits.
+int tiled_fwd_splits(const Shape& s) {
+  const int64_t bn = s.D == 256 ? 32 : 64;
+  const int64_t work = (s.Lq + kFwdBM - 1) / kFwdBM * s.B * s.Hq;
+  const int64_t target = 2 * 256;
+  if (work >= target) return 1;
+  const int64_t nt = (s.Lkv + bn - 1) / bn;
+  int64_t n = (target + work - 1) / work;
+  if (n > nt / 4) n = nt / 4;
+  if (n > 16) n = 16;
+  return n < 1 ? 1 : (int)n;
+}
+
+size_t tiled_fwd_workspace(const Shape& s) {
+  const int n = tiled_fwd_splits(s);
+  if (n == 1) return 0;
+  return (size_t)n * (size_t)(s.B * s.Hq * s.Lq) * (size_t)(s.D + 2) * sizeof(float);
+}
+
 hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
-                            const void* q, const void* k, const void* v, void* o, float* lse, float scale,
+                            const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,
                             hipStream_t st) {
   if (dt == kBF16)
-    return out == kF32 ? launch_d<bf16_t, float>(s, causal, mask, sinks, q, k, v, o, lse, scale, st)
-                       : launch_d<bf16_t, bf16_t>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    return out == kF32 ? launch_d<bf16_t, float>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st)
+                       : launch_d<bf16_t, bf16_t>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
   if (dt == kF16)
-    return out == kF32 ? launch_d<f16_t, float>(s, causal, mask, sinks, q, k, v, o, lse, scale, st)
-                       : launch_d<f16_t, f16_t>(s, causal, mask, sinks, q, k, v, o, lse, scale, st);
+    return out == kF32 ? launch_d<f16_t, float>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st)
+                       : launch_d<f16_t, f16_t>(s, out, causal, mask, sinks, q, k, v, o, lse, scale, ws, st);
   return hipErrorInvalidValue;
 }
 

@@ -41,9 +41,14 @@ hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta
 hipError_t launch_delta(const Shape& s, Dt o_dt, Dt do_dt, const void* o, const void* dO, float* delta,
                         hipStream_t st);
 
-// Tiled forward, 16-bit operands (fwd_tiled.hip).
+// Tiled forward, 16-bit operands (fwd_tiled.hip). When the (query block, head) grid is too
+// small to fill the chip, the keys are split over tiled_fwd_splits(s) workgroups per block,
+// which write unnormalised partials into `ws` (tiled_fwd_workspace(s) bytes:
+// [nsplit][B*Hq*Lq][D] fp32, then [nsplit][B*Hq*Lq] (m, l) pairs) for launch_split_combine.
+int tiled_fwd_splits(const Shape& s);
+size_t tiled_fwd_workspace(const Shape& s);
 hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
-                            const void* q, const void* k, const void* v, void* o, float* lse, float scale,
+                            const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,
                             hipStream_t st);
 
 // Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is the workspace: per (b, hq)
@@ -59,6 +64,12 @@ hipError_t launch_fwd_f32(const Shape& s, bool causal, const Mask& mask, const f
 hipError_t launch_bwd_f32(const Shape& s, bool causal, const Mask& mask, const float* q, const float* k,
                           const float* v, const float* o, const float* lse, const float* dO, float* dq, float* dk,
                           float* dv, float* delta, float scale, int stages, hipStream_t st);
+
+// Merges `nsplit` key-split partials (layout above; m in log2 units of the scaled
+// scores, O unnormalised) into o and lse; the per-head sinks, if any, join here, once
+// (vector_path.hip).
+hipError_t launch_split_combine(const Shape& s, Dt out, int nsplit, const float* part_o, const float* part_ml,
+                                const float* sinks, void* o, float* lse, hipStream_t st);
 
 // Short-query path (vector_path.hip).
 int vector_num_splits(const Shape& s);

@@ -57,7 +57,11 @@ int path_of(int64_t Hq, int64_t Hkv, int64_t Lq, int is_causal, int dtype) {
 size_t delta_bytes(const Shape& s) { return align_up((size_t)(s.B * s.Hq * s.Lq) * sizeof(float)); }
 
 size_t ws_bytes(int backward, const Shape& s, int path) {
-  if (!backward) return path == SDPA_PATH_VECTOR ? align_up(sdpa::vector_fwd_workspace(s)) : 0;
+  if (!backward) {
+    if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_fwd_workspace(s));
+    if (path == SDPA_PATH_TILED) return align_up(sdpa::tiled_fwd_workspace(s));  // key-split partials, small grids
+    return 0;
+  }
   // The vector backward forms Delta inside its kernel; the fp32 path keeps Delta and the
   // tiled path {LSE*log2e, Delta} pairs per query row in the workspace.
   if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_bwd_workspace(s));
@@ -122,7 +126,7 @@ sdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, floa
                                                    v, o, lse, scale, workspace, hs));
     default:
       return device_status(sdpa::launch_fwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, mask, sinks, q, k,
-                                                  v, o, lse, scale, hs));
+                                                  v, o, lse, scale, workspace, hs));
   }
 }
 

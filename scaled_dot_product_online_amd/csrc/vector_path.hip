@@ -706,6 +706,17 @@ __global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __
   Store4<OutT>::run(dq + e4 * 4, x0 * scale, x1 * scale, x2 * scale, x3 * scale);
 }
 
+// The combine kernel over `nsplit` partials [nsplit][B*Hq*Lq][D] and (m, l) pairs.
+template <int D, typename OutT>
+hipError_t combine_typed(const Shape& s, int nsplit, const float* part_o, const float* part_ml, const float* sinks,
+                         void* o, float* lse, hipStream_t st) {
+  const int64_t tr = rows_total(s);
+  constexpr int RPB = kThreads / (D / 4);
+  hipLaunchKernelGGL((vec_combine_kernel<D, OutT>), dim3((unsigned)((tr + RPB - 1) / RPB)), dim3(kThreads), 0, st,
+                     part_o, part_ml, (OutT*)o, lse, tr, nsplit, sinks, (int)s.Hq, (int)s.Lq);
+  return hipGetLastError();
+}
+
 template <typename T, int D, typename OutT>
 hipError_t fwd_typed(const Shape& s, bool causal, const Mask& mask, const float* sinks, const void* q, const void* k,
                      const void* v, void* o, float* lse, float scale, void* ws, hipStream_t st) {
@@ -724,11 +735,7 @@ hipError_t fwd_typed(const Shape& s, bool causal, const Mask& mask, const float*
                      (int)s.Lkv, pl.nsplit, (int)pl.split_len, n_rb, tr, scale_log2, mask, sinks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  constexpr int RPB = kThreads / (D / 4);
-  hipLaunchKernelGGL((vec_combine_kernel<D, OutT>), dim3((unsigned)((tr + RPB - 1) / RPB)), dim3(kThreads), 0, st,
-                     (const float*)part_o, (const float*)part_ml, (OutT*)o, lse, tr, pl.nsplit, sinks, (int)s.Hq,
-                     (int)s.Lq);
-  return hipGetLastError();
+  return combine_typed<D, OutT>(s, pl.nsplit, part_o, part_ml, sinks, o, lse, st);
 }
 
 template <typename T, int D, typename OutT>
@@ -793,6 +800,24 @@ size_t vector_bwd_workspace(const Shape& s) {
                                  : (out == kF32 ? FN<f16_t, 256, float>(__VA_ARGS__) : FN<f16_t, 256, f16_t>(__VA_ARGS__));   \
     default: return hipErrorInvalidValue;                                                                   \
   }
+
+hipError_t launch_split_combine(const Shape& s, Dt out, int nsplit, const float* part_o, const float* part_ml,
+                                const float* sinks, void* o, float* lse, hipStream_t st) {
+#define SDPA_COMBINE(DD)                                                                                   \
+  case DD:                                                                                                 \
+    return out == kF32    ? combine_typed<DD, float>(s, nsplit, part_o, part_ml, sinks, o, lse, st)         \
+           : out == kBF16 ? combine_typed<DD, bf16_t>(s, nsplit, part_o, part_ml, sinks, o, lse, st)        \
+                          : combine_typed<DD, f16_t>(s, nsplit, part_o, part_ml, sinks, o, lse, st);
+  switch (s.D) {
+    SDPA_COMBINE(32)
+    SDPA_COMBINE(64)
+    SDPA_COMBINE(96)
+    SDPA_COMBINE(128)
+    SDPA_COMBINE(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef SDPA_COMBINE
+}
 
 hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
                              const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,

@@ -52,8 +52,14 @@ def test_select_path():
 
 
 def test_workspace_sizes():
-    # tiled and fp32 forward need none; backward keeps Delta (fp32 per query row)
+    # the tiled forward needs none on grids that fill the chip, the fp32 forward none at all;
+    # backward keeps Delta (fp32 per query row)
     assert sd.workspace_bytes(0, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) == 0
+    assert sd.workspace_bytes(0, 8, 8, 8, 128, 128, 64, False, sd.F32) == 0
+    # small tiled grids split the keys: fp32 partials O [nsplit, B*Hq*Lq, D] and (m, l)
+    assert sd.workspace_bytes(0, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == 4 * 8 * 2048 * (64 + 2) * 4
+    assert sd.workspace_bytes(0, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == 2 * 8 * 4096 * (64 + 2) * 4
+    assert sd.workspace_bytes(0, 1, 2, 2, 200, 200, 64, True, sd.F16) == 0  # too few key tiles to split
     assert sd.workspace_bytes(1, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) >= 4 * 32 * 4096 * 4
     assert sd.workspace_bytes(1, 8, 8, 8, 128, 128, 64, False, sd.F32) >= 8 * 8 * 128 * 4
     # vector path: split partials
