@@ -23,6 +23,10 @@
 //   column), which puts P and dS directly in the B-operand layout of
 //   dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are read with the LDS
 //   transpose read.
+// Small grids (fewer workgroups than the chip holds at once): kernel 1 splits its key
+//   tiles and kernel 2 its (query head, query tile) sequence over several workgroups,
+//   which write fp32 partials of dQ (resp. dK and dV); a reduction kernel sums them in a
+//   fixed order (deterministic) and applies the scale.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -77,15 +81,19 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
                                                          const uint16_t* __restrict__ dO, OutT* __restrict__ dq,
                                                          f32x2_t* __restrict__ rowstat, int Hq, int G, int Lq,
                                                          int Lkv, int n_qblk, int n_bh, int lq_pad,
-                                                         float scale_log2, float scale, Mask mask) {
+                                                         float scale_log2, float scale, Mask mask, int nsplit,
+                                                         int split_tiles, float* __restrict__ dq_part) {
   using TL = SwzTile<D>;
   constexpr int kDqBN = dq_bn<D>();
   constexpr int TILE = kDqBN * TL::RB;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];  // [buffer][K, V]
 
-  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh, G);
-  int qblk = wid / n_bh;
-  const int bh = wid - qblk * n_bh;
+  // Work id: query block major, then key split, then (b, hq) (as the forward).
+  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh * nsplit, G);
+  int qblk = wid / (n_bh * nsplit);
+  const int rest = wid - qblk * (n_bh * nsplit);
+  const int split = rest / n_bh;
+  const int bh = rest - split * n_bh;
   if (CAUSAL) qblk = n_qblk - 1 - qblk;
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hk = hq / G, Hkv = Hq / G;
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
   if (HAS_MASK && lse2 == -INFINITY) lse2 = INFINITY;
   const int64_t mrow =
       HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
-  if (row_ok && g == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, dlt};
+  if (row_ok && g == 0 && split == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, dlt};
 
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -136,6 +144,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
   const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
   const int kv_end = CAUSAL ? min(Lkv, qblk * kDqBM + kDqBM + co) : Lkv;
   const int ntiles = (kv_end + kDqBN - 1) / kDqBN;
+  const int t_lo = split * split_tiles, t_hi = min(ntiles, t_lo + split_tiles);  // this split's key tiles
   const int key_lim = CAUSAL ? min(Lkv, qrow + 1 + co) : Lkv;
   const int G16 = lane >> 4, L16 = lane & 15;
   const int fk0 = TL::f(n);
@@ -251,12 +260,15 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
 
   const srd_t rk = make_srd(k + kvoff, (uint32_t)Lkv * D * 2);
   const srd_t rv = make_srd(v + kvoff, (uint32_t)Lkv * D * 2);
-  TL::template dma_fill<kDqBN>(rk, lds, 0, wave, 4, lane);
-  TL::template dma_fill<kDqBN>(rv, lds + TILE, 0, wave, 4, lane);
-  for (int t = 0; t < ntiles; ++t) {
+  if (t_lo < t_hi) {
+    uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
+    TL::template dma_fill<kDqBN>(rk, b0, t_lo * kDqBN, wave, 4, lane);
+    TL::template dma_fill<kDqBN>(rv, b0 + TILE, t_lo * kDqBN, wave, 4, lane);
+  }
+  for (int t = t_lo; t < t_hi; ++t) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < ntiles) {
+    if (t + 1 < t_hi) {
       uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
       TL::template dma_fill<kDqBN>(rk, nb, (t + 1) * kDqBN, wave, 4, lane);
       TL::template dma_fill<kDqBN>(rv, nb + TILE, (t + 1) * kDqBN, wave, 4, lane);
@@ -266,6 +278,18 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
     const int kt0 = t * kDqBN;
     if (CAUSAL && kt0 > q0 + 31 + co) continue;
     tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0 + co), kt, vt, kt0);  // wave-uniform flag
+  }
+  if (dq_part != nullptr) {  // one key split: fp32 partial of dQ / scale, [split][b*Hq*Lq + hq*Lq + q]
+    if (row_ok) {
+      float* po = dq_part + (((int64_t)split * n_bh + bh) * Lq + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4_t*)(po + db * 32 + 8 * r4 + 4 * g) =
+              (f32x4_t){acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
+    }
+    return;
   }
   if (row_ok) {
     OutT* out = dq + qoff + (int64_t)qrow * D;
@@ -293,7 +317,9 @@ constexpr int kv_waves() {
 }
 constexpr int kKvBM = 64;  // queries per tile
 
-template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
+// SPLIT: one of several workgroups that share a key block's (head, query tile) sequence
+// and write fp32 partials (a separate instantiation, so that the unsplit kernel is unchanged).
+template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT, bool SPLIT>
 __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_per_eu(kv_waves<D>() / 4, kv_waves<D>() / 4))) void dkv_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
@@ -301,7 +327,9 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
                                                             const f32x2_t* __restrict__ rowstat,
                                                             OutT* __restrict__ dk, OutT* __restrict__ dv, int Hq,
                                                             int G, int Lq, int Lkv, int n_kblk, int n_bhk,
-                                                            int lq_pad, float scale_log2, float scale, Mask mask) {
+                                                            int lq_pad, float scale_log2, float scale, Mask mask,
+                                                            int nsplit, float* __restrict__ dk_part,
+                                                            float* __restrict__ dv_part) {
   using TL = SwzTile<D, 16>;
   constexpr int kKvWaves = kv_waves<D>();
   constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
@@ -311,10 +339,13 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
 
   // Low block ids carry the key blocks that see the most causal queries (dispatched
-  // first). With n_bhk a multiple of 8, dispatch id % 8 == bhk % 8: each XCD keeps to
-  // its own KV groups.
-  const int kblk = blockIdx.x / n_bhk;
-  const int bhk = blockIdx.x - kblk * n_bhk;
+  // first), then the split, then the KV group. With n_bhk a multiple of 8, dispatch
+  // id % 8 == bhk % 8: each XCD keeps to its own KV groups.
+  const int nsp = SPLIT ? nsplit : 1;
+  const int kblk = blockIdx.x / (n_bhk * nsp);
+  const int rest = blockIdx.x - kblk * (n_bhk * nsp);
+  const int split = SPLIT ? rest / n_bhk : 0;
+  const int bhk = rest - split * n_bhk;
   const int Hkv = Hq / G, b = bhk / Hkv, hk = bhk - b * Hkv;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int n16 = lane & 15, q4 = lane >> 4;
@@ -355,6 +386,9 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   // the workgroups that run at once stream the same Q / dO tiles and share them in L2.
   const int total = G * ntiles;
   auto tile_of = [&](int it) { return q_begin + (ntiles - 1 - it / G) * kKvBM; };
+  // This split's part of the sequence (all of it without splits).
+  const int per = SPLIT ? (total + nsplit - 1) / nsplit : total;
+  const int it_lo = SPLIT ? min(total, split * per) : 0, it_hi = SPLIT ? min(total, it_lo + per) : total;
   const int L16 = lane & 15;
   const int fa0 = TL::f(n16);            // 16-byte reads: row qm*16 + n16
   const int trow = 4 * q4 + (L16 >> 2);  // transposed reads: rows 32c' + trow (+16)
@@ -512,17 +546,29 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     }
   };
 
-  if (total > 0) issue(0, lds);
-  for (int it = 0; it < total; ++it) {
+  if (it_lo < it_hi) issue(it_lo, lds + (it_lo & 1) * BUF);
+  for (int it = it_lo; it < it_hi; ++it) {
     wait_vmem();
     __syncthreads();
-    if (it + 1 < total) issue(it + 1, lds + ((it + 1) & 1) * BUF);
+    if (it + 1 < it_hi) issue(it + 1, lds + ((it + 1) & 1) * BUF);
     const uint8_t* qt = lds + (it & 1) * BUF;
     const uint8_t* dt = qt + TILE;
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = tile_of(it);
     if (CAUSAL && t0 + kKvBM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
     tile((t0 + kKvBM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G);  // wave-uniform flag
+  }
+  if constexpr (SPLIT) {  // one split: fp32 partials of dK / scale and dV, [split][b*Hkv*Lkv + hk*Lkv + key]
+    if (krow < Lkv) {
+      const int64_t po = ((int64_t)split * n_bhk + bhk) * Lkv * D + (int64_t)krow * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const int d = db * 16 + 4 * q4;
+        *(f32x4_t*)(dk_part + po + d) = dka[db];
+        *(f32x4_t*)(dv_part + po + d) = dva[db];
+      }
+    }
+    return;
   }
   if (krow < Lkv) {
     const int64_t ko = kvoff + (int64_t)krow * D;
@@ -535,74 +581,128 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   }
 }
 
+// Splits of the two kernels (small grids only). dQ: as the forward, enough workgroups for
+// two per CU, at least 4 key tiles per split on average. dK/dV (one workgroup per CU):
+// enough for one per CU, at least 4 (head, query tile) steps per split. At most 16.
+int split_count(int64_t work, int64_t target, int64_t steps) {
+  if (work >= target) return 1;
+  int64_t n = (target + work - 1) / work;
+  if (n > steps / 4) n = steps / 4;
+  if (n > 16) n = 16;
+  return n < 1 ? 1 : (int)n;
+}
+int dq_splits(const Shape& s) {
+  const int64_t bn = s.D == 256 ? 32 : 64;
+  return split_count((s.Lq + kDqBM - 1) / kDqBM * s.B * s.Hq, 2 * 256, (s.Lkv + bn - 1) / bn);
+}
+int dkv_splits(const Shape& s) {
+  const int64_t bn = s.D == 256 ? 64 : 128;  // 16 keys per wave
+  return split_count((s.Lkv + bn - 1) / bn * s.B * s.Hkv, 256, (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM));
+}
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+// Workspace: {LSE*log2e, Delta} pairs, then (split grids) the dQ partials, then the dK and
+// dV partials.
+size_t rowstat_bytes(const Shape& s) { return align256((size_t)(s.B * s.Hq * tiled_rowstat_stride(s.Lq)) * 8); }
+size_t dq_part_bytes(const Shape& s) {
+  const int n = dq_splits(s);
+  return n > 1 ? align256((size_t)n * (size_t)(s.B * s.Hq * s.Lq * s.D) * 4) : 0;
+}
+size_t dkv_part_bytes(const Shape& s) {  // each of dK, dV
+  const int n = dkv_splits(s);
+  return n > 1 ? align256((size_t)n * (size_t)(s.B * s.Hkv * s.Lkv * s.D) * 4) : 0;
+}
+
 template <typename T, int D, bool C, bool M, typename OutT>
-hipError_t launch_typed(const Shape& s, const Mask& mask, const void* q, const void* k, const void* v, const void* o,
-                        const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws, float scale,
-                        int stages, hipStream_t st) {
+hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws,
+                        float scale, int stages, hipStream_t st) {
   f32x2_t* rowstat = (f32x2_t*)ws;  // [B*Hq][lq_pad] {LSE*log2e, Delta}
   const int lq_pad = (int)tiled_rowstat_stride(s.Lq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int G = (int)(s.Hq / s.Hkv);
+  char* parts = (char*)ws + rowstat_bytes(s);
   if (stages & kStage0) {
     const int n_qblk = (int)((s.Lq + kDqBM - 1) / kDqBM);
     const int n_bh = (int)(s.B * s.Hq);
-    hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh), dim3(kThreads), 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse, (const uint16_t*)dO, (OutT*)dq,
-                       rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, lq_pad, scale_log2, scale, mask);
+    const int nsplit = dq_splits(s);
+    constexpr int BN = dq_bn<D>();
+    const int nt = (int)((s.Lkv + BN - 1) / BN);
+    float* dq_part = nsplit > 1 ? (float*)parts : nullptr;
+    hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kThreads), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
+                       (const uint16_t*)dO, (OutT*)dq, rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh,
+                       lq_pad, scale_log2, scale, mask, nsplit, (nt + nsplit - 1) / nsplit, dq_part);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && nsplit > 1) e = launch_split_reduce(s, out, nsplit, dq_part, dq, s.B * s.Hq * s.Lq, scale, st);
     if (e != hipSuccess) return e;
   }
   if (!(stages & kStage1)) return hipSuccess;
   constexpr int kKvBN = 16 * kv_waves<D>();
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
-  hipLaunchKernelGGL((dkv_kernel<T, D, C, M, OutT>), dim3(n_kblk * n_bhk), dim3(64 * kv_waves<D>()), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO,
-                     (const f32x2_t*)rowstat, (OutT*)dk, (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk,
-                     n_bhk, lq_pad, scale_log2, scale, mask);
-  return hipGetLastError();
+  const int nsplit = dkv_splits(s);
+  float* dk_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s)) : nullptr;
+  float* dv_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s) + dkv_part_bytes(s)) : nullptr;
+  auto kern = nsplit > 1 ? dkv_kernel<T, D, C, M, OutT, true> : dkv_kernel<T, D, C, M, OutT, false>;
+  hipLaunchKernelGGL(kern, dim3(n_kblk * n_bhk * nsplit), dim3(64 * kv_waves<D>()), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, (const f32x2_t*)rowstat, (OutT*)dk,
+                     (OutT*)dv, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_kblk, n_bhk, lq_pad, scale_log2, scale, mask,
+                     nsplit, dk_part, dv_part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const int64_t kv_rows = s.B * s.Hkv * s.Lkv;
+  e = launch_split_reduce(s, out, nsplit, dk_part, dk, kv_rows, scale, st);
+  if (e != hipSuccess) return e;
+  return launch_split_reduce(s, out, nsplit, dv_part, dv, kv_rows, 1.f, st);
 }
 
 template <typename T, int D, typename OutT>
-hipError_t launch_mode(const Shape& s, bool causal, const Mask& mask, const void* q, const void* k, const void* v,
-                       const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws,
-                       float scale, int stages, hipStream_t st) {
+hipError_t launch_mode(const Shape& s, Dt out, bool causal, const Mask& mask, const void* q, const void* k,
+                       const void* v, const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       float* ws, float scale, int stages, hipStream_t st) {
   if (causal)
-    return launch_typed<T, D, true, false, OutT>(s, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
+    return launch_typed<T, D, true, false, OutT>(s, out, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages,
+                                                 st);
   if (mask.kind != kMaskNone)
-    return launch_typed<T, D, false, true, OutT>(s, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
-  return launch_typed<T, D, false, false, OutT>(s, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
+    return launch_typed<T, D, false, true, OutT>(s, out, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages,
+                                                 st);
+  return launch_typed<T, D, false, false, OutT>(s, out, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages,
+                                                st);
 }
 
 template <typename T, typename OutT>
-hipError_t launch_d(const Shape& s, bool causal, const Mask& mask, const void* q, const void* k, const void* v,
-                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* delta,
+hipError_t launch_d(const Shape& s, Dt out, bool causal, const Mask& mask, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws,
                     float scale, int stages, hipStream_t st) {
+#define SDPA_BWD_D(DD) \
+  case DD: return launch_mode<T, DD, OutT>(s, out, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
   switch (s.D) {
-    case 32: return launch_mode<T, 32, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
-    case 64: return launch_mode<T, 64, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
-    case 96: return launch_mode<T, 96, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
-    case 128:
-      return launch_mode<T, 128, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
-    case 256:
-      return launch_mode<T, 256, OutT>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+    SDPA_BWD_D(32)
+    SDPA_BWD_D(64)
+    SDPA_BWD_D(96)
+    SDPA_BWD_D(128)
+    SDPA_BWD_D(256)
     default: return hipErrorInvalidValue;
   }
+#undef SDPA_BWD_D
 }
 
 }  // namespace
 
+size_t tiled_bwd_workspace(const Shape& s) { return rowstat_bytes(s) + dq_part_bytes(s) + 2 * dkv_part_bytes(s); }
+
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
                             const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
-                            void* dk, void* dv, float* delta, float scale, int stages, hipStream_t st) {
+                            void* dk, void* dv, float* ws, float scale, int stages, hipStream_t st) {
   if (dt == kBF16)
     return out == kF32
-               ? launch_d<bf16_t, float>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
-               : launch_d<bf16_t, bf16_t>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+               ? launch_d<bf16_t, float>(s, out, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
+               : launch_d<bf16_t, bf16_t>(s, out, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages,
+                                          st);
   if (dt == kF16)
     return out == kF32
-               ? launch_d<f16_t, float>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st)
-               : launch_d<f16_t, f16_t>(s, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, delta, scale, stages, st);
+               ? launch_d<f16_t, float>(s, out, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st)
+               : launch_d<f16_t, f16_t>(s, out, causal, mask, q, k, v, o, lse, dO, dq, dk, dv, ws, scale, stages, st);
   return hipErrorInvalidValue;
 }
 

@@ -51,12 +51,14 @@ hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Ma
                             const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,
                             hipStream_t st);
 
-// Tiled backward, 16-bit operands (bwd_tiled.hip). `delta` is the workspace: per (b, hq)
-// a row of tiled_rowstat_stride(Lq) {LSE*log2e, Delta} fp32 pairs.
+// Tiled backward, 16-bit operands (bwd_tiled.hip). `ws` is the workspace of
+// tiled_bwd_workspace(s) bytes: first, per (b, hq), a row of tiled_rowstat_stride(Lq)
+// {LSE*log2e, Delta} fp32 pairs; then, on small grids, fp32 partials of dQ and of dK, dV.
 inline int64_t tiled_rowstat_stride(int64_t Lq) { return (Lq + 63) / 64 * 64; }
+size_t tiled_bwd_workspace(const Shape& s);
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
                             const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
-                            void* dk, void* dv, float* delta, float scale, int stages, hipStream_t st);
+                            void* dk, void* dv, float* ws, float scale, int stages, hipStream_t st);
 
 // float32 path (fp32_path.hip).
 hipError_t launch_fwd_f32(const Shape& s, bool causal, const Mask& mask, const float* sinks, const float* q,
@@ -70,6 +72,11 @@ hipError_t launch_bwd_f32(const Shape& s, bool causal, const Mask& mask, const f
 // (vector_path.hip).
 hipError_t launch_split_combine(const Shape& s, Dt out, int nsplit, const float* part_o, const float* part_ml,
                                 const float* sinks, void* o, float* lse, hipStream_t st);
+
+// out[r, :] = scale * sum_s part[s, r, :] for `rows` rows of s.D elements, summed in split
+// order, stored as `out` (vector_path.hip).
+hipError_t launch_split_reduce(const Shape& s, Dt out, int nsplit, const float* part, void* out_ptr, int64_t rows,
+                               float scale, hipStream_t st);
 
 // Short-query path (vector_path.hip).
 int vector_num_splits(const Shape& s);

@@ -65,7 +65,7 @@ size_t ws_bytes(int backward, const Shape& s, int path) {
   // The vector backward forms Delta inside its kernel; the fp32 path keeps Delta and the
   // tiled path {LSE*log2e, Delta} pairs per query row in the workspace.
   if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_bwd_workspace(s));
-  if (path == SDPA_PATH_TILED) return align_up((size_t)(s.B * s.Hq * sdpa::tiled_rowstat_stride(s.Lq)) * 8);
+  if (path == SDPA_PATH_TILED) return align_up(sdpa::tiled_bwd_workspace(s));  // + split partials, small grids
   return delta_bytes(s);
 }
 

@@ -819,6 +819,33 @@ hipError_t launch_split_combine(const Shape& s, Dt out, int nsplit, const float*
 #undef SDPA_COMBINE
 }
 
+hipError_t launch_split_reduce(const Shape& s, Dt out, int nsplit, const float* part, void* out_ptr, int64_t rows,
+                               float scale, hipStream_t st) {
+  const int64_t n4 = rows * (s.D / 4);
+  const dim3 grid((unsigned)((n4 + kThreads - 1) / kThreads));
+#define SDPA_REDUCE(DD)                                                                                          \
+  case DD:                                                                                                       \
+    if (out == kF32)                                                                                             \
+      hipLaunchKernelGGL((vec_dq_reduce_kernel<DD, float>), grid, dim3(kThreads), 0, st, part, (float*)out_ptr, \
+                         rows, nsplit, scale);                                                                   \
+    else if (out == kBF16)                                                                                       \
+      hipLaunchKernelGGL((vec_dq_reduce_kernel<DD, bf16_t>), grid, dim3(kThreads), 0, st, part,                 \
+                         (bf16_t*)out_ptr, rows, nsplit, scale);                                                 \
+    else                                                                                                         \
+      hipLaunchKernelGGL((vec_dq_reduce_kernel<DD, f16_t>), grid, dim3(kThreads), 0, st, part, (f16_t*)out_ptr, \
+                         rows, nsplit, scale);                                                                   \
+    return hipGetLastError();
+  switch (s.D) {
+    SDPA_REDUCE(32)
+    SDPA_REDUCE(64)
+    SDPA_REDUCE(96)
+    SDPA_REDUCE(128)
+    SDPA_REDUCE(256)
+    default: return hipErrorInvalidValue;
+  }
+#undef SDPA_REDUCE
+}
+
 hipError_t launch_fwd_vector(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const float* sinks,
                              const void* q, const void* k, const void* v, void* o, float* lse, float scale, void* ws,
                              hipStream_t st) {

@@ -60,6 +60,11 @@ def test_workspace_sizes():
     assert sd.workspace_bytes(0, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == 4 * 8 * 2048 * (64 + 2) * 4
     assert sd.workspace_bytes(0, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == 2 * 8 * 4096 * (64 + 2) * 4
     assert sd.workspace_bytes(0, 1, 2, 2, 200, 200, 64, True, sd.F16) == 0  # too few key tiles to split
+    # ... and so does the backward: {LSE*log2e, Delta} pairs, dQ partials (4 key splits), dK and dV
+    # partials (2 splits of the query tiles)
+    rows, kv = 8 * 2048, 8 * 2048
+    assert sd.workspace_bytes(1, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == rows * 8 + 4 * rows * 64 * 4 + 2 * (
+        2 * kv * 64 * 4)
     assert sd.workspace_bytes(1, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) >= 4 * 32 * 4096 * 4
     assert sd.workspace_bytes(1, 8, 8, 8, 128, 128, 64, False, sd.F32) >= 8 * 8 * 128 * 4
     # vector path: split partials

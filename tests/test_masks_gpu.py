@@ -38,6 +38,7 @@ for _dt in ("f16", "bf16"):
         (1, 4, 2, 150, 170, 128, _dt, True, None, None, 0, True),            # causal + sinks
         (1, 4, 2, 130, 900, 128, _dt, False, "bool", "full", 2, True),       # tiled, 3 key splits
         (1, 2, 1, 100, 800, 64, _dt, True, None, None, 0, True),             # causal + sinks, 3 key splits
+        (1, 8, 2, 256, 300, 128, _dt, False, "bool", "keypad", 0, True),     # dK/dV in 4 splits
         (2, 8, 2, 4, 1000, 64, _dt, False, "bool", "full", 1, True),         # short-query
         (2, 16, 4, 8, 4099, 128, _dt, False, "additive", "keypad", 0, True),  # several splits
         (2, 8, 2, 7, 333, 128, _dt, False, None, None, 0, True),

@@ -59,11 +59,14 @@ for _dt in ("f16", "bf16"):
         (2, 4, 1, 70, 300, 96, _dt, False),     # tiled, ragged
         (2, 8, 2, 7, 1000, 96, _dt, False),     # vector
         (2, 16, 4, 8, 4099, 96, _dt, True),     # vector, causal, several splits
-        # tiled forward with keys split over workgroups (grids under two workgroups per CU)
+        # keys split over workgroups on small grids: tiled forward and dQ (and dK/dV where noted)
         (1, 2, 1, 150, 1100, 64, _dt, False),   # 4 splits, ragged last tile
         (1, 4, 2, 200, 1000, 128, _dt, True),   # 4 splits, causal with Lq < Lkv
         (1, 2, 2, 640, 640, 64, _dt, True),     # 2 splits, the second empty for the first query blocks
         (1, 2, 1, 96, 700, 96, _dt, False),     # 2 splits, head dim 96
+        # backward splits on small grids: dK/dV over its (query head, query tile) sequence
+        (1, 8, 1, 512, 256, 64, _dt, False),    # 16 splits, GQA 8:1
+        (1, 4, 1, 256, 200, 256, _dt, False),   # 4 splits, head dim 256 (4-wave workgroups)
         # head dim 256 (32-key forward / dQ tiles, 4-wave dK/dV, 2-wave short-query kernels)
         (1, 4, 2, 200, 200, 256, _dt, True),    # tiled, causal
         (1, 4, 1, 70, 300, 256, _dt, False),    # tiled, ragged
