@@ -37,9 +37,6 @@ constexpr Mask kNoMask = {nullptr, kMaskNone, 0, 0, 0, 0};
 hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es,
                             const float* sinks, float* dsinks, hipStream_t st);
 
-// Delta_i = sum_d dO[i,d] * O[i,d] over all B*Hq*Lq rows (delta.hip).
-hipError_t launch_delta(const Shape& s, Dt o_dt, Dt do_dt, const void* o, const void* dO, float* delta,
-                        hipStream_t st);
 
 // Tiled forward, 16-bit operands (fwd_tiled.hip). When the (query block, head) grid is too
 // small to fill the chip, the keys are split over tiled_fwd_splits(s) workgroups per block,
