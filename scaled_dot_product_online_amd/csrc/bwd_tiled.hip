@@ -265,6 +265,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
     TL::template dma_fill<kDqBN>(rk, b0, t_lo * kDqBN, wave, 4, lane);
     TL::template dma_fill<kDqBN>(rv, b0 + TILE, t_lo * kDqBN, wave, 4, lane);
   }
+  // Key padding: tiles whose keys are all padding are skipped (mask bytes read a tile ahead).
+  const bool pad = HAS_MASK && is_key_padding(mask);
+  uint32_t kept_next = pad && t_lo < t_hi ? key_kept(mask, b, t_lo * kDqBN, kDqBN, Lkv, lane) : 1u;
   for (int t = t_lo; t < t_hi; ++t) {
     wait_vmem();
     __syncthreads();
@@ -273,10 +276,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
       TL::template dma_fill<kDqBN>(rk, nb, (t + 1) * kDqBN, wave, 4, lane);
       TL::template dma_fill<kDqBN>(rv, nb + TILE, (t + 1) * kDqBN, wave, 4, lane);
     }
+    const uint32_t kept = kept_next;
+    if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * kDqBN, kDqBN, Lkv, lane);
     const uint8_t* kt = lds + (t & 1) * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     const int kt0 = t * kDqBN;
     if (CAUSAL && kt0 > q0 + 31 + co) continue;
+    if (pad && !__any(kept != 0u)) continue;  // every key of the tile is padding
     tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0 + co), kt, vt, kt0);  // wave-uniform flag
   }
   if (dq_part != nullptr) {  // one key split: fp32 partial of dQ / scale, [split][b*Hq*Lq + hq*Lq + q]
@@ -416,6 +422,8 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   // With a mask: element offset of (this tile's query head, query 0, key krow); rows are
   // added per query (clamped into range: out-of-range entries are zeroed by the edge test).
   const int64_t mkey = HAS_MASK ? (int64_t)b * mask.sb + (int64_t)min(krow, Lkv - 1) : 0;
+  // A key-padding mask that removes all 16 keys of this wave leaves dK = dV = 0: no tile work.
+  const bool wave_keys = !(HAS_MASK && is_key_padding(mask)) || __any(key_kept(mask, b, kw0, 16, Lkv, lane) != 0u);
   auto tile = [&](bool masked, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0, int hq) {
     // Lane constants made opaque per tile, so that the compiler recomputes the LDS
     // addresses derived from them inside the loop instead of keeping each one live.
@@ -556,6 +564,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = tile_of(it);
     if (CAUSAL && t0 + kKvBM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
+    if (!wave_keys) continue;
     tile((t0 + kKvBM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G);  // wave-uniform flag
   }
   if constexpr (SPLIT) {  // one split: fp32 partials of dK / scale and dV, [split][b*Hkv*Lkv + hk*Lkv + key]

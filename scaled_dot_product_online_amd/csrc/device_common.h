@@ -313,6 +313,7 @@ __device__ __forceinline__ void mask_bias4_log2(const void* p, int kind, int64_t
   }
 }
 __device__ __forceinline__ float load_f32(const bf16_t* p) { return to_f32<bf16_t>(p->bits); }
+
 __device__ __forceinline__ float load_f32(const f16_t* p) { return to_f32<f16_t>(p->bits); }
 
 }  // namespace sdpa

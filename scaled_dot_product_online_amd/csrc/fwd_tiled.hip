@@ -131,6 +131,10 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     TL::template dma_fill<kFwdBN>(rk, b0, t_lo * kFwdBN, wave, 4, lane);
     TL::template dma_fill<kFwdBN>(rv, b0 + TILE, t_lo * kFwdBN, wave, 4, lane);
   }
+  // Key padding: a tile whose keys are all padding adds nothing and is skipped; its mask
+  // bytes are read one tile ahead.
+  const bool pad = MASKED && is_key_padding(mask);
+  uint32_t kept_next = pad && t_lo < t_hi ? key_kept(mask, b, t_lo * kFwdBN, kFwdBN, Lkv, lane) : 1u;
   for (int t = t_lo; t < t_hi; ++t) {
     wait_vmem();
     __syncthreads();  // tile t is in LDS; every wave has finished tile t - 1
@@ -139,10 +143,13 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
       TL::template dma_fill<kFwdBN>(rk, nb, (t + 1) * kFwdBN, wave, 4, lane);
       TL::template dma_fill<kFwdBN>(rv, nb + TILE, (t + 1) * kFwdBN, wave, 4, lane);
     }
+    const uint32_t kept = kept_next;
+    if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * kFwdBN, kFwdBN, Lkv, lane);
     const uint8_t* kt = lds + (t & 1) * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     const int kt0 = t * kFwdBN;
     if (CAUSAL && kt0 > q0 + 31 + co) continue;  // tile entirely above this wave's diagonal
+    if (pad && !__any(kept != 0u)) continue;  // every key of the tile is padding
 
     // S^T = K Q^T: 32 keys x 32 queries per accumulator block.
     f32x16_t s[kFwdBN / 32];

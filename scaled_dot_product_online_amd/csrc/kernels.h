@@ -32,6 +32,18 @@ struct Mask {
 };
 constexpr Mask kNoMask = {nullptr, kMaskNone, 0, 0, 0, 0};
 
+// A boolean mask that varies only along keys (key padding: query and head strides 0).
+__device__ __forceinline__ bool is_key_padding(const Mask& mask) {
+  return mask.kind == kMaskBool && mask.sq == 0 && mask.sh == 0;
+}
+// For such a mask: this lane's key key0 + lane of batch b, nonzero when kept (lanes >= n
+// and keys past the end read 0). A kernel loads the bytes of its next key tile one step
+// ahead and tests them with __any() when it gets there.
+__device__ __forceinline__ uint32_t key_kept(const Mask& mask, int b, int key0, int n, int Lkv, int lane) {
+  const int key = key0 + lane;
+  return (lane < n && key < Lkv) ? ((const uint8_t*)mask.p)[(int64_t)b * mask.sb + key] : 0u;
+}
+
 // dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * Delta(b,h,i), with Delta(b,h,i) at
 // delta[((b*Hq + h) * pitch + i) * es] (delta.hip). One deterministic reduction per head.
 hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es,

@@ -39,6 +39,11 @@ for _dt in ("f16", "bf16"):
         (1, 4, 2, 130, 900, 128, _dt, False, "bool", "full", 2, True),       # tiled, 3 key splits
         (1, 2, 1, 100, 800, 64, _dt, True, None, None, 0, True),             # causal + sinks, 3 key splits
         (1, 8, 2, 256, 300, 128, _dt, False, "bool", "keypad", 0, True),     # dK/dV in 4 splits
+        # contiguous key padding (batch b keeps its first keys, one batch none): whole key
+        # tiles and whole dK/dV waves are padding, which the tiled kernels skip
+        (3, 4, 2, 130, 600, 128, _dt, False, "bool", "padded", 0, False),
+        (3, 4, 1, 100, 700, 64, _dt, False, "bool", "padded", 0, True),
+        (3, 4, 2, 80, 500, 256, _dt, False, "bool", "padded", 0, False),
         (2, 8, 2, 4, 1000, 64, _dt, False, "bool", "full", 1, True),         # short-query
         (2, 16, 4, 8, 4099, 128, _dt, False, "additive", "keypad", 0, True),  # several splits
         (2, 8, 2, 7, 333, 128, _dt, False, None, None, 0, True),
@@ -63,7 +68,10 @@ def _inputs(c, seed):
     B, Hq, Hkv, Lq, Lkv, D, dt, causal, kind, spec, empty, sinks = c
     case = inp.make_case(B, Hq, Hkv, Lq, Lkv, D, dt, is_causal=causal, seed=seed)
     mask = None
-    if kind is not None:
+    if spec == "padded":  # batch 0 keeps Lkv - 150 keys, batch 1 none, batch b > 1 Lkv - 150 - 97 b
+        keep = [0 if b == 1 else max(0, Lkv - 150 - 97 * b) for b in range(B)]
+        mask = ("bool", inp.make_key_padding_mask(B, Lkv, keep))
+    elif kind is not None:
         mask = (kind, inp.make_mask(kind, _mask_shape(spec, B, Hq, Lq, Lkv), dt, seed=seed + 7, empty_rows=empty))
     sk = inp.make_sinks(Hq, seed=seed + 3, none_heads=(Hq - 1,)) if sinks else None
     return case, mask, sk
