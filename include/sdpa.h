@@ -101,7 +101,10 @@ int sdpa_select_path(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D
  * tiled path when its grid of (128-query block, head) pairs is too small to give
  * every compute unit two workgroups: there the keys are split over several
  * workgroups whose fp32 partials (unnormalised O, running max, row sum) the
- * workspace holds until a second kernel merges them.
+ * workspace holds until a second kernel merges them. The backward always needs one
+ * (per-row statistics that its first stage leaves for the second); on small grids
+ * it also holds the fp32 partials of dQ, dK and dV of split kernels, which a
+ * reduction sums in a fixed order.
  */
 size_t sdpa_workspace_bytes(int backward, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv,
                             int64_t D, int is_causal, sdpa_dtype_t dtype);
