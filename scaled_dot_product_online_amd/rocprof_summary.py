@@ -9,6 +9,9 @@
 --calib-bytes  size of the plain device copy the program ran (bench.py --calibrate-copy):
            the counters' KiB for that copy, against its true bytes read and written,
            give the factors that turn FETCH_SIZE / WRITE_SIZE into bytes.
+--bench-log    stdout of the traced bench.py run: its own HIP-event times per stage (timed
+           steps only; the trace's averages also hold the warm-up calls) are listed beside
+           the durations.
 
 Writes profiles/NAME.md (per-kernel durations, and per-dispatch HBM traffic when
 counter runs are given) and, for the traffic, profiles/NAME.traffic.json keyed by
@@ -67,6 +70,7 @@ def main():
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calib-bytes", type=int, default=0)
+    ap.add_argument("--bench-log")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
 
@@ -77,6 +81,19 @@ def main():
     for r in stats:
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    if a.bench_log:
+        with open(a.bench_log) as f:
+            runs = [json.loads(l) for l in f if l.startswith("{")]
+        lines += ["", "HIP-event times that bench.py measured in the same traced run (timed steps only; the "
+                      "averages above also hold the warm-up calls):", "",
+                  "| workload | stage | ms per call |", "|---|---|---|"]
+        for r in runs:
+            for stage, ms in r["kernel_ms"].items():
+                lines.append(f"| {r['config']['workload']} | {stage} | {ms:.4f} |")
+            vp = r.get("vector_path")
+            if vp:
+                for stage, ms in vp["kernel_ms"].items():
+                    lines.append(f"| {vp['workload']} | {stage} | {ms:.4f} |")
     traffic = None
     if a.fetch and a.write:
         fetch, write = counter_means(a.fetch), counter_means(a.write)
