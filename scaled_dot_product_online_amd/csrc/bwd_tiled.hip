@@ -592,7 +592,10 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
 
 // Splits of the two kernels (small grids only). dQ: as the forward, enough workgroups for
 // two per CU, at least 4 key tiles per split on average. dK/dV (one workgroup per CU):
-// enough for one per CU, at least 4 (head, query tile) steps per split. At most 16.
+// enough for one per CU, at least 4 (head, query tile) steps per split. At most 16. Under a
+// causal mask dK/dV aims for two per CU: the key blocks near the end see few query tiles,
+// so about half of its split workgroups have little work (measured faster; the same for dQ
+// measured slower).
 int split_count(int64_t work, int64_t target, int64_t steps) {
   if (work >= target) return 1;
   int64_t n = (target + work - 1) / work;
@@ -604,9 +607,10 @@ int dq_splits(const Shape& s) {
   const int64_t bn = s.D == 256 ? 32 : 64;
   return split_count((s.Lq + kDqBM - 1) / kDqBM * s.B * s.Hq, 2 * 256, (s.Lkv + bn - 1) / bn);
 }
-int dkv_splits(const Shape& s) {
+int dkv_splits(const Shape& s, bool causal) {
   const int64_t bn = s.D == 256 ? 64 : 128;  // 16 keys per wave
-  return split_count((s.Lkv + bn - 1) / bn * s.B * s.Hkv, 256, (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM));
+  return split_count((s.Lkv + bn - 1) / bn * s.B * s.Hkv, (causal ? 2 : 1) * 256,
+                     (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM));
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace: {LSE*log2e, Delta} pairs, then (split grids) the dQ partials, then the dK and
@@ -616,8 +620,8 @@ size_t dq_part_bytes(const Shape& s) {
   const int n = dq_splits(s);
   return n > 1 ? align256((size_t)n * (size_t)(s.B * s.Hq * s.Lq * s.D) * 4) : 0;
 }
-size_t dkv_part_bytes(const Shape& s) {  // each of dK, dV
-  const int n = dkv_splits(s);
+size_t dkv_part_bytes(const Shape& s, bool causal) {  // each of dK, dV
+  const int n = dkv_splits(s, causal);
   return n > 1 ? align256((size_t)n * (size_t)(s.B * s.Hkv * s.Lkv * s.D) * 4) : 0;
 }
 
@@ -649,9 +653,9 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q,
   constexpr int kKvBN = 16 * kv_waves<D>();
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
-  const int nsplit = dkv_splits(s);
+  const int nsplit = dkv_splits(s, C);
   float* dk_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s)) : nullptr;
-  float* dv_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s) + dkv_part_bytes(s)) : nullptr;
+  float* dv_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s) + dkv_part_bytes(s, C)) : nullptr;
   auto kern = nsplit > 1 ? dkv_kernel<T, D, C, M, OutT, true> : dkv_kernel<T, D, C, M, OutT, false>;
   hipLaunchKernelGGL(kern, dim3(n_kblk * n_bhk * nsplit), dim3(64 * kv_waves<D>()), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, (const f32x2_t*)rowstat, (OutT*)dk,
@@ -698,7 +702,9 @@ hipError_t launch_d(const Shape& s, Dt out, bool causal, const Mask& mask, const
 
 }  // namespace
 
-size_t tiled_bwd_workspace(const Shape& s) { return rowstat_bytes(s) + dq_part_bytes(s) + 2 * dkv_part_bytes(s); }
+size_t tiled_bwd_workspace(const Shape& s, bool causal) {
+  return rowstat_bytes(s) + dq_part_bytes(s) + 2 * dkv_part_bytes(s, causal);
+}
 
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
                             const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,

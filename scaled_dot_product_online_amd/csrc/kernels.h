@@ -61,10 +61,10 @@ hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Ma
                             hipStream_t st);
 
 // Tiled backward, 16-bit operands (bwd_tiled.hip). `ws` is the workspace of
-// tiled_bwd_workspace(s) bytes: first, per (b, hq), a row of tiled_rowstat_stride(Lq)
+// tiled_bwd_workspace(s, causal) bytes: first, per (b, hq), a row of tiled_rowstat_stride(Lq)
 // {LSE*log2e, Delta} fp32 pairs; then, on small grids, fp32 partials of dQ and of dK, dV.
 inline int64_t tiled_rowstat_stride(int64_t Lq) { return (Lq + 63) / 64 * 64; }
-size_t tiled_bwd_workspace(const Shape& s);
+size_t tiled_bwd_workspace(const Shape& s, bool causal);
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,
                             const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
                             void* dk, void* dv, float* ws, float scale, int stages, hipStream_t st);

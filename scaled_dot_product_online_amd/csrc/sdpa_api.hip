@@ -56,7 +56,7 @@ int path_of(int64_t Hq, int64_t Hkv, int64_t Lq, int is_causal, int dtype) {
 
 size_t delta_bytes(const Shape& s) { return align_up((size_t)(s.B * s.Hq * s.Lq) * sizeof(float)); }
 
-size_t ws_bytes(int backward, const Shape& s, int path) {
+size_t ws_bytes(int backward, const Shape& s, int path, bool causal) {
   if (!backward) {
     if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_fwd_workspace(s));
     if (path == SDPA_PATH_TILED) return align_up(sdpa::tiled_fwd_workspace(s));  // key-split partials, small grids
@@ -65,7 +65,7 @@ size_t ws_bytes(int backward, const Shape& s, int path) {
   // The vector backward forms Delta inside its kernel; the fp32 path keeps Delta and the
   // tiled path {LSE*log2e, Delta} pairs per query row in the workspace.
   if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_bwd_workspace(s));
-  if (path == SDPA_PATH_TILED) return align_up(sdpa::tiled_bwd_workspace(s));  // + split partials, small grids
+  if (path == SDPA_PATH_TILED) return align_up(sdpa::tiled_bwd_workspace(s, causal));  // + split partials, small grids
   return delta_bytes(s);
 }
 
@@ -110,7 +110,7 @@ sdpa_status_t run_fwd(const void* q, const void* k, const void* v, void* o, floa
   if (((uintptr_t)sinks & 3u) != 0) return SDPA_ERR_ALIGN;
   const Shape s{B, Hq, Hkv, Lq, Lkv, D};
   const int path = path_of(Hq, Hkv, Lq, is_causal, dtype);
-  const size_t need = ws_bytes(0, s, path);
+  const size_t need = ws_bytes(0, s, path, is_causal != 0);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
     if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return SDPA_ERR_ALIGN;
@@ -143,7 +143,7 @@ size_t sdpa_workspace_bytes(int backward, int64_t B, int64_t Hq, int64_t Hkv, in
                             int is_causal, sdpa_dtype_t dtype) {
   if (check_shape(B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype, dtype) != SDPA_OK) return (size_t)-1;
   const Shape s{B, Hq, Hkv, Lq, Lkv, D};
-  return ws_bytes(backward, s, path_of(Hq, Hkv, Lq, is_causal, dtype));
+  return ws_bytes(backward, s, path_of(Hq, Hkv, Lq, is_causal, dtype), is_causal != 0);
 }
 
 sdpa_status_t sdpa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
@@ -186,7 +186,7 @@ sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, c
     if (!aligned16(p)) return SDPA_ERR_ALIGN;
   const Shape s{B, Hq, Hkv, Lq, Lkv, D};
   const int path = path_of(Hq, Hkv, Lq, is_causal, dtype);
-  const size_t need = ws_bytes(1, s, path);
+  const size_t need = ws_bytes(1, s, path, is_causal != 0);
   if (!workspace || workspace_bytes < need) return SDPA_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return SDPA_ERR_ALIGN;
   hipStream_t hs = (hipStream_t)stream;

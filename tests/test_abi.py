@@ -59,6 +59,11 @@ def test_workspace_sizes():
     # small tiled grids split the keys: fp32 partials O [nsplit, B*Hq*Lq, D] and (m, l)
     assert sd.workspace_bytes(0, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == 4 * 8 * 2048 * (64 + 2) * 4
     assert sd.workspace_bytes(0, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == 2 * 8 * 4096 * (64 + 2) * 4
+    # causal dK/dV splits aim for two workgroups per CU: L = 4096 now splits its query tiles 2 ways
+    rows = 8 * 4096
+    assert sd.workspace_bytes(1, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == rows * 8 + 2 * rows * 64 * 4 + 2 * (
+        2 * rows * 64 * 4)
+    assert sd.workspace_bytes(1, 1, 8, 8, 4096, 4096, 64, False, sd.F16) == rows * 8 + 2 * rows * 64 * 4
     assert sd.workspace_bytes(0, 1, 2, 2, 200, 200, 64, True, sd.F16) == 0  # too few key tiles to split
     # ... and so does the backward: {LSE*log2e, Delta} pairs, dQ partials (4 key splits), dK and dV
     # partials (2 splits of the query tiles)
