@@ -51,6 +51,8 @@
  *             surface at the caller's next synchronisation, as for any stream
  *             operation. All outputs are fully overwritten (dk and dv are not
  *             accumulated into).
+ * Scale       Any finite value, including 0 (every visible key weighs the same) and
+ *             negative values; a non-finite scale is SDPA_ERR_VALUE.
  * Threads     No mutable global state; calls are thread-safe.
  */
 #ifndef SDPA_MI355X_H
@@ -96,7 +98,10 @@ int sdpa_select_path(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D
 
 /*
  * Bytes of workspace sdpa_fwd (backward = 0) or sdpa_bwd (backward = 1) needs
- * for these sizes; 0 if none. Pure host function. Returns (size_t)-1 when the
+ * for these sizes; 0 if none. Pure host function. The workspace is caller-owned
+ * device memory that the library uses in place and never allocates itself, as the
+ * pages' kernels take the caller's tensors' buffers directly (mps-flash-sdpa 0.1.0,
+ * "How It Works": zero-copy buffer handoff to the kernels). Returns (size_t)-1 when the
  * sizes are invalid. The forward needs one on the short-query path, and on the
  * tiled path when its grid of (128-query block, head) pairs is too small to give
  * every compute unit two workgroups: there the keys are split over several

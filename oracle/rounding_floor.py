@@ -36,7 +36,11 @@ This is not the oracle: ``sdpa_reference`` is the definition, and a parity test
 never passes on this model alone (its bound always includes the distance to the
 definition). Pins: ``round_to`` against IEEE conversions and exhaustive bf16
 spacing checks; with ``op_dtype = out_dtype = "f64"`` the model reproduces the
-definition exactly (tests/test_oracle_pins.py).
+definition exactly; at 16 bits the backward's error stays within the rigorous
+per-element bounds of its two roundings, has the size that rounding-error theory
+predicts for them, vanishes when every rounded operand is representable, and responds
+to the stored output through Delta as the first-order formula says
+(tests/test_oracle_pins.py).
 """
 
 from __future__ import annotations
@@ -137,6 +141,19 @@ def emulate_forward(q, k, v, scale, is_causal, op_dtype, out_dtype, kv_block, kv
     return o
 
 
+# The backward's two operand roundings, named so that a test can check each one's effect
+# (tests/test_oracle_pins.py plants a slip in them and sees it caught): the probabilities
+# enter the dV product rounded to the operand type; dS enters the dQ and dK products
+# rounded to the operand type *before* the scale is applied (the kernels multiply the
+# fp32 accumulators by the scale once, at the end).
+def round_p(p, op_dtype):
+    return round_to(p, op_dtype)
+
+
+def round_ds(ds, op_dtype, scale):
+    return round_to(ds, op_dtype)
+
+
 def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, b, hk, mask=None):
     """Modelled dQ [G,Lq,D], dK, dV [Lkv,D] of KV group (b, hk), rounded to ``out_dtype``.
 
@@ -167,12 +184,35 @@ def emulate_backward_group(q, k, v, do, o_stored, lse, scale, is_causal, op_dtyp
         delta = np.sum(doh * np.asarray(o_stored[b, h], dtype=np.float64), axis=1)
         dp = doh @ vh.T
         ds = p * (dp - delta[:, None])
-        rp = round_to(p, op_dtype)
-        rds = round_to(ds, op_dtype)
+        rp = round_p(p, op_dtype)
+        rds = round_ds(ds, op_dtype, scale)
         dv += rp.T @ doh
         dq[g] = float(scale) * (rds @ kh)
         dk += float(scale) * (rds.T @ qh)
     return round_to(dq, out_dtype), round_to(dk, out_dtype), round_to(dv, out_dtype)
+
+
+def emulate_dq_rows(qh, kh, vh, doh, o_stored, lse, scale, is_causal, op_dtype, rows, bias=None):
+    """Modelled dQ (before its final rounding) of query rows ``rows`` of one head.
+
+    ``o_stored`` and ``lse`` are the stored output and logsumexp of those rows. The
+    rounding points are those of ``emulate_backward_group``: Delta from the stored
+    output, dS rounded to the operand type before the product with K, then the scale."""
+    qh, kh, vh, doh = (np.asarray(a, dtype=np.float64) for a in (qh, kh, vh, doh))
+    rows = np.asarray(rows)
+    Lq, Lkv = qh.shape[0], kh.shape[0]
+    s = (qh[rows] @ kh.T) * float(scale)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)[rows]
+    lse = np.asarray(lse, dtype=np.float64)[:, None]
+    with np.errstate(invalid="ignore"):
+        p = np.where(np.isfinite(lse), np.exp(s - lse), 0.0)
+    if is_causal:
+        p = np.where(np.arange(Lkv)[None, :] <= rows[:, None] + (Lkv - Lq), p, 0.0)
+    do = doh[rows]
+    delta = np.sum(do * np.asarray(o_stored, dtype=np.float64), axis=1)
+    ds = p * (do @ vh.T - delta[:, None])
+    return float(scale) * (round_ds(ds, op_dtype, scale) @ kh)
 
 
 def emulate_backward(q, k, v, do, o_stored, lse, scale, is_causal, op_dtype, out_dtype, mask=None):

@@ -120,6 +120,94 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous [B, H, L, D]")
 
 
+_HEAD_DIMS = (32, 64, 96, 128, 256)
+
+
+def check_eligible(q, k, v, is_causal=False, attn_mask=None, sinks=None):
+    """Raise ValueError naming the first reason the library cannot take these inputs.
+
+    Types, shapes and dtypes are checked first, the devices last (every tensor on the GPU
+    of q), so that nothing reaches the C ABI that could make a kernel read or write
+    outside a buffer."""
+    import torch
+
+    dtypes = (torch.float32, torch.float16, torch.bfloat16)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} is not a tensor")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}; supported: float32, float16, bfloat16")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, L, D], got shape {tuple(t.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError(f"q, k, v dtypes differ: {q.dtype}, {k.dtype}, {v.dtype}")
+    B, Hq, Lq, D = q.shape
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} in batch or head size")
+    Hkv = k.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"query heads {Hq} are not a multiple of key/value heads {Hkv}")
+    if D not in _HEAD_DIMS:
+        raise ValueError(f"head size {D} is not supported (supported: {_HEAD_DIMS})")
+    if is_causal and Lq > k.shape[2]:
+        raise ValueError("causal attention needs Lq <= Lkv (sequences aligned at their ends)")
+    if attn_mask is not None:
+        if is_causal:
+            raise ValueError("attn_mask and is_causal are not combined")
+        if not isinstance(attn_mask, torch.Tensor):
+            raise ValueError("attn_mask must be a tensor")
+        if attn_mask.dtype not in (torch.bool, q.dtype):
+            raise ValueError(f"attn_mask must be bool or {q.dtype}, got {attn_mask.dtype}")
+        if attn_mask.requires_grad:
+            raise ValueError("no gradient is formed for attn_mask")
+        try:
+            torch.broadcast_shapes(tuple(attn_mask.shape), (B, Hq, Lq, k.shape[2]))
+        except RuntimeError:
+            raise ValueError(f"attn_mask {tuple(attn_mask.shape)} does not broadcast to {(B, Hq, Lq, k.shape[2])}")
+    if sinks is not None:
+        if not isinstance(sinks, torch.Tensor):
+            raise ValueError("sinks must be a tensor")
+        if sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,):
+            raise ValueError(f"sinks must be float32 of shape ({Hq},)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("attn_mask", attn_mask), ("sinks", sinks)):
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}; the library runs on the GPU only")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+
+
+def check_buffer(name, t, shape, dtype, device):
+    """Raise ValueError unless ``t`` is a contiguous tensor of exactly this shape and dtype on ``device``."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} is not a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _workspace_arg(workspace, need, device):
+    """(pointer, size in bytes) of a caller's workspace, checked against the size the call needs."""
+    if workspace is None:
+        return None
+    if not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes; this call needs {need}")
+    return nbytes
+
+
 def mask_args(attn_mask, B, Hq, Lq, Lkv, dtype_code):
     """(kind, tensor, stride_b, stride_h, stride_q) for a torch mask broadcastable to [B,Hq,Lq,Lkv].
 
@@ -169,6 +257,7 @@ def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True
     [B,Hq,Lq,Lkv]; ``sinks`` is a float32 [Hq] tensor of per-head sink logits."""
     import torch
 
+    check_eligible(q, k, v, is_causal, attn_mask, sinks)
     _contig(q, k, v)
     B, Hq, Lq, D = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
@@ -178,15 +267,19 @@ def sdpa_fwd(q, k, v, scale=None, is_causal=False, out_dtype=None, need_lse=True
         scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
     if out is None:
         out = torch.empty((B, Hq, Lq, D), dtype=_torch_dtype(odt), device=q.device)
+    check_buffer("out", out, (B, Hq, Lq, D), _torch_dtype(odt), q.device)
     if need_lse and lse is None:
         lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
     if not need_lse:
         lse = None
+    if lse is not None:
+        check_buffer("lse", lse, (B, Hq, Lq), torch.float32, q.device)
     nws = workspace_bytes(0, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
     if workspace is None and nws > 0:
         workspace = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    ws_len = _workspace_arg(workspace, nws, q.device) or 0
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)))
-    tail = (dt, odt, _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(q.device, stream))
+    tail = (dt, odt, _ptr(workspace), ws_len, _stream(q.device, stream))
     if attn_mask is None and sinks is None:
         st = library().sdpa_fwd(*head, *tail)
     else:
@@ -207,7 +300,8 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
     without sinks."""
     import torch
 
-    _contig(q, k, v, o, lse, dO)
+    check_eligible(q, k, v, is_causal, attn_mask, sinks)
+    _contig(q, k, v)
     B, Hq, Lq, D = q.shape
     Hkv, Lkv = k.shape[1], k.shape[2]
     dt = _torch_code(q.dtype)
@@ -215,15 +309,24 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
     if scale is None:
         scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
     tdt = _torch_dtype(odt)
+    check_buffer("o", o, (B, Hq, Lq, D), tdt, q.device)
+    check_buffer("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    check_buffer("dO", dO, (B, Hq, Lq, D), q.dtype, q.device)
     dq = torch.empty((B, Hq, Lq, D), dtype=tdt, device=q.device) if dq is None else dq
     dk = torch.empty((B, Hkv, Lkv, D), dtype=tdt, device=q.device) if dk is None else dk
     dv = torch.empty((B, Hkv, Lkv, D), dtype=tdt, device=q.device) if dv is None else dv
+    check_buffer("dq", dq, (B, Hq, Lq, D), tdt, q.device)
+    check_buffer("dk", dk, (B, Hkv, Lkv, D), tdt, q.device)
+    check_buffer("dv", dv, (B, Hkv, Lkv, D), tdt, q.device)
+    if sinks is not None and dsinks is not None:
+        check_buffer("dsinks", dsinks, (Hq,), torch.float32, q.device)
     nws = workspace_bytes(1, B, Hq, Hkv, Lq, Lkv, D, is_causal, dt)
     if workspace is None:
         workspace = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
+    ws_len = _workspace_arg(workspace, nws, q.device)
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv),
             B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)))
-    tail = (dt, odt, _ptr(workspace), workspace.numel(), _stream(q.device, stream))
+    tail = (dt, odt, _ptr(workspace), ws_len, _stream(q.device, stream))
     if attn_mask is None and sinks is None:
         st = library().sdpa_bwd(*head, *tail) if stage is None else library().sdpa_bwd_stage(int(stage), *head, *tail)
         _check(st)
@@ -239,3 +342,4 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
         st = library().sdpa_bwd_masked_stage(int(stage), *head, *masked, *tail)
     _check(st)
     return dq, dk, dv, (dsinks if sk is not None else None)
+

@@ -23,56 +23,8 @@ import torch
 
 from . import _lib
 
-_DTYPES = (torch.float32, torch.float16, torch.bfloat16)
-_HEAD_DIMS = (32, 64, 96, 128, 256)
-
-
-def check_eligible(q, k, v, is_causal=False, attn_mask=None, sinks=None):
-    """Raise ValueError naming the first reason the library cannot take these tensors."""
-    ts = {"q": q, "k": k, "v": v}
-    for name, t in ts.items():
-        if not isinstance(t, torch.Tensor):
-            raise ValueError(f"{name} is not a tensor")
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} is on {t.device}; the library runs on the GPU only")
-        if t.dtype not in _DTYPES:
-            raise ValueError(f"{name} has dtype {t.dtype}; supported: float32, float16, bfloat16")
-        if t.dim() != 4:
-            raise ValueError(f"{name} must be [B, H, L, D], got shape {tuple(t.shape)}")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError(f"q, k, v dtypes differ: {q.dtype}, {k.dtype}, {v.dtype}")
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k, v are on different devices")
-    B, Hq, Lq, D = q.shape
-    if k.shape != v.shape:
-        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ")
-    if k.shape[0] != B or k.shape[3] != D:
-        raise ValueError(f"k/v {tuple(k.shape)} do not match q {tuple(q.shape)} in batch or head size")
-    Hkv = k.shape[1]
-    if Hkv < 1 or Hq % Hkv:
-        raise ValueError(f"query heads {Hq} are not a multiple of key/value heads {Hkv}")
-    if D not in _HEAD_DIMS:
-        raise ValueError(f"head size {D} is not supported (supported: {_HEAD_DIMS})")
-    if is_causal and Lq > k.shape[2]:
-        raise ValueError("causal attention needs Lq <= Lkv (sequences aligned at their ends)")
-    if attn_mask is not None:
-        if is_causal:
-            raise ValueError("attn_mask and is_causal are not combined")
-        if not isinstance(attn_mask, torch.Tensor) or attn_mask.device != q.device:
-            raise ValueError("attn_mask must be a tensor on the device of q")
-        if attn_mask.dtype not in (torch.bool, q.dtype):
-            raise ValueError(f"attn_mask must be bool or {q.dtype}, got {attn_mask.dtype}")
-        if attn_mask.requires_grad:
-            raise ValueError("no gradient is formed for attn_mask")
-        try:
-            torch.broadcast_shapes(tuple(attn_mask.shape), (B, Hq, Lq, k.shape[2]))
-        except RuntimeError:
-            raise ValueError(f"attn_mask {tuple(attn_mask.shape)} does not broadcast to {(B, Hq, Lq, k.shape[2])}")
-    if sinks is not None:
-        if not isinstance(sinks, torch.Tensor) or sinks.device != q.device:
-            raise ValueError("sinks must be a tensor on the device of q")
-        if sinks.dtype != torch.float32 or tuple(sinks.shape) != (Hq,):
-            raise ValueError(f"sinks must be float32 of shape ({Hq},)")
+# The eligibility rules live with the binding, which applies them on every call.
+check_eligible = _lib.check_eligible
 
 
 class _Attention(torch.autograd.Function):

@@ -103,6 +103,26 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // 2^kRescaleSlack and the O rescale is skipped for most tiles.
 constexpr float kRescaleSlack = 8.0f;
 
+// ---- the sign of the scale ---------------------------------------------------------------
+// The forward kernels take the row maximum of the scaled scores by scaling the maximum of
+// the raw ones, and mask keys with -inf before scaling. Both need a factor > 0. A negative
+// scale is therefore applied as |scale| to Q with its sign bits flipped, and a zero scale
+// as 1 to Q = 0: either way each score is exactly scale * (Q K^T) (a sign flip of 16-bit
+// operands is exact, and the fp32 sums are symmetric under it), every masked key stays
+// -inf, and the kernel's multiplier is positive.
+struct QSign {
+  float scale_log2;  // the factor the kernel uses, > 0
+  uint32_t keep, flip;
+  __device__ __forceinline__ u32x4_t apply(u32x4_t x) const {
+    return (u32x4_t){(x[0] & keep) ^ flip, (x[1] & keep) ^ flip, (x[2] & keep) ^ flip, (x[3] & keep) ^ flip};
+  }
+};
+__device__ __forceinline__ QSign q_sign(float scale_log2) {
+  if (scale_log2 == 0.f) return QSign{1.f, 0u, 0u};
+  if (scale_log2 < 0.f) return QSign{-scale_log2, ~0u, 0x80008000u};
+  return QSign{scale_log2, ~0u, 0u};
+}
+
 // ---- dispatch order ------------------------------------------------------------------
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
 // Map dispatch id i to a work id so that, within every run of 8*chunk dispatch

@@ -79,9 +79,13 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
   const rsrc_t rq = make_rsrc(q + (int64_t)bh * Lq * D, (uint32_t)Lq * D * 2);
 
   // Q^T as the B operand: lane (n, g) holds Q[qrow][16c + 8g .. +7] (rows past Lq read as zero).
+  // The scale is folded into Q's sign: the kernel only ever multiplies scores by a positive
+  // factor, so that the row maximum and the -inf of masked keys are taken on scaled scores.
   u32x4_t qop[D / 16];
+  const QSign qs = q_sign(scale_log2);
+  scale_log2 = qs.scale_log2;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) qop[c] = buf_load16(rq, (uint32_t)((qrow * D + 16 * c + 8 * g) * 2));
+  for (int c = 0; c < D / 16; ++c) qop[c] = qs.apply(buf_load16(rq, (uint32_t)((qrow * D + 16 * c + 8 * g) * 2)));
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) settle(qop[c]);
 

@@ -101,9 +101,12 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
   // Q^T as the B operand: lane (n, g) holds packed row rb*32 + n, d = 16c + 8g .. +7
   // (rows past the group's G*Lq read as zero).
   const rsrc_t rq = make_rsrc(q + (row0 + rb * 32) * D, (uint32_t)max(0, rows - rb * 32) * D * 2);
+  // The scale's sign is folded into Q (see q_sign), so scores are only scaled by a factor > 0.
   u32x4_t qop[D / 16];
+  const QSign qs = q_sign(scale_log2);
+  scale_log2 = qs.scale_log2;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) qop[c] = buf_load16(rq, (uint32_t)((n * D + 16 * c + 8 * g) * 2));
+  for (int c = 0; c < D / 16; ++c) qop[c] = qs.apply(buf_load16(rq, (uint32_t)((n * D + 16 * c + 8 * g) * 2)));
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) settle(qop[c]);
 

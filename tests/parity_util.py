@@ -3,7 +3,7 @@
 The GPU result is compared element by element with the fp64 oracle on the same
 seeded inputs. Bound per element x of output tensor X (tests/golden/tolerances.json):
 
-    |x_gpu - x_oracle| <= tol_X + F_X + R_X + ulp_out(x) / 2,
+    |x_gpu - x_oracle| <= tol_X + F_X + ulp_out(x) / 2,
     F_X = max|X_model_pre - X_oracle|
 
 where tol_X is the stated tolerance for the operand dtype and direction, X_model_pre
@@ -12,12 +12,16 @@ kernels' key-block size) before its final rounding to the output dtype, and
 ulp_out(x) / 2 is that final rounding at the element (the larger magnitude of the two
 values decides the binade). The pages' tolerances were measured against attention in
 the same dtype (mps-flash-sdpa 0.1.0, "Gradient Correctness"), whose outputs carry that
-rounding too. R_X (backward only) is the spread that the rounding of the stored forward
-output alone causes: the backward forms Delta_i = sum_d dO_id O_id from the O it is
-given, and which neighbour each element of the kernel's stored O took is not the
-model's; R is the largest difference between the backward model driven by the model's
-stored O and by the exact O rounded to the output dtype (two such roundings). For fp32
-operands F and R are ~1e-7, so the fp32 bound is about the literal 1e-5.
+rounding too.
+
+The backward is checked on decoupled inputs: it receives the oracle's O rounded to the
+output dtype and the oracle's LSE rounded to fp32 (not the GPU forward's), and the model
+is driven by exactly those, so the bound needs no allowance for which neighbour the
+forward's stored output took. One end-to-end check (the backward fed by the GPU
+forward) keeps that allowance, R_X: the largest difference between the backward model
+driven by the model's stored O and by the exact O rounded to the output dtype (two
+roundings of the same O, which Delta_i = sum_d dO_id O_id sees). For fp32 operands F
+and R are ~1e-7, so the fp32 bound is about the literal 1e-5.
 """
 
 from __future__ import annotations
@@ -66,10 +70,21 @@ def oracle_mask(case, mask):
     return np.asarray(arr, dtype=bool) if kind == "bool" else inp.as_float64(arr, case.dtype)
 
 
-def run_gpu(case, out_dtype, device, backward=True, mask=None, sinks=None):
+def fed_tensors(want, case, out_dtype, device):
+    """The oracle's O (rounded to out_dtype) and LSE (fp32) as device tensors for sdpa_bwd."""
+    import torch
+
+    o = inp.to_torch(inp.from_f32(np.asarray(want["o_fed"], dtype=np.float32), out_dtype), out_dtype, device)
+    lse = torch.from_numpy(np.asarray(want["lse_fed"], dtype=np.float32)).to(device)
+    return o, lse
+
+
+def run_gpu(case, out_dtype, device, backward=True, mask=None, sinks=None, fed=None):
     """Run sdpa_fwd (and sdpa_bwd) through the C ABI; returns float64 numpy arrays.
 
-    mask: None or (kind, storage array) from inputs.make_mask; sinks: float32 [Hq] or None."""
+    mask: None or (kind, storage array) from inputs.make_mask; sinks: float32 [Hq] or None.
+    fed: None (the backward takes the GPU forward's O and LSE: end to end), or the dict
+    that ``reference`` returned, whose ``o_fed`` / ``lse_fed`` the backward then takes."""
     import torch
 
     import scaled_dot_product_online_amd as sd
@@ -80,13 +95,17 @@ def run_gpu(case, out_dtype, device, backward=True, mask=None, sinks=None):
     ts = None if sinks is None else torch.from_numpy(np.ascontiguousarray(sinks, dtype=np.float32)).to(device)
     extra = f" mask={mask[0]}{tuple(mask[1].shape)}" if mask is not None else ""
     extra += " sinks" if sinks is not None else ""
+    extra += f" scale={case.scale:g}"
     print(f"[gpu] fwd {case.shape_str} out={out_dtype}{extra}", flush=True)
     o, lse = sd.sdpa_fwd(q, k, v, scale=case.scale, is_causal=case.is_causal, out_dtype=tdt, attn_mask=tm, sinks=ts)
     torch.cuda.synchronize()
     res = {"o": inp.from_torch(o, out_dtype), "lse": inp.from_torch(lse, "f32")}
     if backward:
         do = inp.to_torch(case.do, case.dtype, device)
-        print(f"[gpu] bwd {case.shape_str} out={out_dtype}{extra}", flush=True)
+        if fed is not None:
+            o, lse = fed_tensors(fed, case, out_dtype, device)
+        print(f"[gpu] bwd {case.shape_str} out={out_dtype}{extra} {'decoupled' if fed is not None else 'end-to-end'}",
+              flush=True)
         g = sd.sdpa_bwd(q, k, v, o, lse, do, scale=case.scale, is_causal=case.is_causal, out_dtype=tdt, attn_mask=tm,
                         sinks=ts)
         torch.cuda.synchronize()
@@ -97,33 +116,48 @@ def run_gpu(case, out_dtype, device, backward=True, mask=None, sinks=None):
     return res
 
 
-def reference(case, out_dtype, backward=True, mask=None, sinks=None):
-    """Oracle values and the rounding-model values for the whole case."""
+def _op_dtype(case):
+    return case.dtype if case.dtype != "f32" else "f32"
+
+
+def reference(case, out_dtype, backward=True, mask=None, sinks=None, end_to_end=False):
+    """Oracle values and the rounding-model values for the whole case.
+
+    The backward model is driven by ``o_fed`` / ``lse_fed`` (the oracle's O rounded to
+    out_dtype, its LSE rounded to fp32), which run_gpu(fed=...) hands to the GPU backward.
+    With ``end_to_end`` it is driven instead by the model's own stored forward output, as
+    the GPU backward is when it takes the GPU forward's, and R (``*_spread``) is added."""
     q, k, v = case.f64("q"), case.f64("k"), case.f64("v")
     m = oracle_mask(case, mask)
     sk = None if sinks is None else np.asarray(sinks, dtype=np.float64)
     o, lse = ref.attention_forward(q, k, v, case.scale, case.is_causal, mask=m, sinks=sk)
-    op = case.dtype if case.dtype != "f32" else "f32"
+    op = _op_dtype(case)
     pn = path_name(case)
-    o_model = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, out_dtype, KV_BLOCK[pn], slack=SLACK[pn],
-                                 mask=m, sinks=sk)
     o_pre = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, "f64", KV_BLOCK[pn], slack=SLACK[pn],
                                mask=m, sinks=sk)
-    out = {"o": o, "lse": lse, "o_model": o_pre, "out_dtype": out_dtype}
+    o_fed, lse_fed = rf.round_to(o, out_dtype), rf.round_to(lse, "f32")
+    out = {"o": o, "lse": lse, "o_model": o_pre, "out_dtype": out_dtype, "o_fed": o_fed, "lse_fed": lse_fed}
     if backward:
         do = case.f64("do")
         dq, dk, dv = ref.attention_backward(q, k, v, do, case.scale, case.is_causal, mask=m, sinks=sk)
-        # The kernels form Delta from their stored (rounded) output: the model does too.
-        mdq, mdk, mdv = rf.emulate_backward(q, k, v, do, o_model, lse, case.scale, case.is_causal, op, "f64",
-                                            mask=m)
-        alt = rf.emulate_backward(q, k, v, do, rf.round_to(o, out_dtype), lse, case.scale, case.is_causal, op, "f64",
-                                  mask=m)
-        out.update(dq=dq, dk=dk, dv=dv, dq_model=mdq, dk_model=mdk, dv_model=mdv,
-                   **{n + "_spread": float(np.abs(a - b).max()) for n, a, b in zip(("dq", "dk", "dv"), (mdq, mdk, mdv),
-                                                                                    alt)})
+        out.update(dq=dq, dk=dk, dv=dv)
+        if end_to_end:
+            # The kernels form Delta from their stored (rounded) output: the model does too.
+            o_model = rf.round_to(o_pre, out_dtype)
+            mdq, mdk, mdv = rf.emulate_backward(q, k, v, do, o_model, lse, case.scale, case.is_causal, op, "f64",
+                                                mask=m)
+            alt = rf.emulate_backward(q, k, v, do, o_fed, lse, case.scale, case.is_causal, op, "f64", mask=m)
+            out.update({n + "_spread": float(np.abs(a - b).max())
+                        for n, a, b in zip(("dq", "dk", "dv"), (mdq, mdk, mdv), alt)})
+            o_sink, lse_sink = o_model, lse
+        else:
+            mdq, mdk, mdv = rf.emulate_backward(q, k, v, do, o_fed, lse_fed, case.scale, case.is_causal, op, "f64",
+                                                mask=m)
+            o_sink, lse_sink = o_fed, lse_fed
+        out.update(dq_model=mdq, dk_model=mdk, dv_model=mdv)
         if sk is not None:
             out["dsinks"] = ref.sink_gradient(q, k, v, do, case.scale, case.is_causal, sk, mask=m)
-            out["dsinks_model"], out["dsinks_mag"] = rf.emulate_sink_gradient(do, o_model, lse, sk)
+            out["dsinks_model"], out["dsinks_mag"] = rf.emulate_sink_gradient(do, o_sink, lse_sink, sk)
     return out
 
 
@@ -178,8 +212,9 @@ def reference_group(case, out_dtype, b, hk, backward=True, mask=None, sinks=None
     """Oracle and model values for the G query heads of KV group (b, hk) only.
 
     Used at full workload sizes, where the whole-tensor oracle would take minutes.
-    Returns arrays shaped like the group's slices: o/lse/dq [G, Lq, ...], dk/dv [Lkv, D].
-    (dsinks sums over every batch, so a group cannot check it.)
+    Returns arrays shaped like the group's slices: o/lse/dq [G, Lq, ...], dk/dv [Lkv, D],
+    and ``o_fed`` / ``lse_fed`` for the group (the backward model is driven by them, as in
+    ``reference``). (dsinks sums over every batch, so a group cannot check it.)
     """
     G = case.Hq // case.Hkv
     hs = slice(hk * G, (hk + 1) * G)
@@ -191,22 +226,65 @@ def reference_group(case, out_dtype, b, hk, backward=True, mask=None, sinks=None
     o, lse = ref.attention_forward(q, k, v, case.scale, case.is_causal, mask=m, sinks=sk)
     op = case.dtype
     pn = path_name(case)
-    o_model = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, out_dtype, KV_BLOCK[pn], slack=SLACK[pn],
-                                 mask=m, sinks=sk)
     o_pre = rf.emulate_forward(q, k, v, case.scale, case.is_causal, op, "f64", KV_BLOCK[pn], slack=SLACK[pn],
                                mask=m, sinks=sk)
-    out = {"o": o[0], "lse": lse[0], "o_model": o_pre[0], "out_dtype": out_dtype}
+    o_fed, lse_fed = rf.round_to(o, out_dtype), rf.round_to(lse, "f32")
+    out = {"o": o[0], "lse": lse[0], "o_model": o_pre[0], "out_dtype": out_dtype, "o_fed": o_fed[0],
+           "lse_fed": lse_fed[0]}
     if backward:
         do = inp.as_float64(case.do[b:b + 1, hs], case.dtype)
         dq, dk, dv = ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0, mask=m, sinks=sk)
-        mdq, mdk, mdv = rf.emulate_backward_group(q, k, v, do, o_model, lse, case.scale, case.is_causal, op,
+        mdq, mdk, mdv = rf.emulate_backward_group(q, k, v, do, o_fed, lse_fed, case.scale, case.is_causal, op,
                                                   "f64", 0, 0, mask=m)
-        alt = rf.emulate_backward_group(q, k, v, do, rf.round_to(o, out_dtype), lse, case.scale, case.is_causal, op,
-                                        "f64", 0, 0, mask=m)
-        out.update(dq=dq, dk=dk, dv=dv, dq_model=mdq, dk_model=mdk, dv_model=mdv,
-                   **{n + "_spread": float(np.abs(a - b).max()) for n, a, b in zip(("dq", "dk", "dv"), (mdq, mdk, mdv),
-                                                                                    alt)})
+        out.update(dq=dq, dk=dk, dv=dv, dq_model=mdq, dk_model=mdk, dv_model=mdv)
     return out
+
+
+def reference_rows(case, out_dtype, b, h, rows, mask=None, sinks=None):
+    """Oracle and model values of query rows ``rows`` of head (b, h): O, LSE and dQ.
+
+    dQ of a row depends only on that row's O and LSE (through Delta_i and P_i), so the
+    backward model of these rows is driven by ``o_fed`` / ``lse_fed`` of the same rows."""
+    G = case.Hq // case.Hkv
+    hk = h // G
+    rows = np.asarray(rows)
+    qh = inp.as_float64(case.q[b, h], case.dtype)
+    kh = inp.as_float64(case.k[b, hk], case.dtype)
+    vh = inp.as_float64(case.v[b, hk], case.dtype)
+    doh = inp.as_float64(case.do[b, h], case.dtype)
+    mk = oracle_mask(case, mask)
+    bias = None if mk is None else ref.head_bias(mk, case.B, case.Hq, case.Lq, case.Lkv, b, h)
+    sink = None if sinks is None else float(sinks[h])
+    o, lse, _ = ref.head_forward(qh, kh, vh, case.scale, case.is_causal, rows, bias=bias, sink=sink)
+    dq, _, _, _ = ref.head_backward(qh, kh, vh, doh, case.scale, case.is_causal, rows, bias=bias, sink=sink)
+    pn = path_name(case)
+    o_pre = rf.emulate_forward_head(qh, kh, vh, case.scale, case.is_causal, case.dtype, "f64", KV_BLOCK[pn],
+                                    rows=rows, slack=SLACK[pn], bias=bias, sink=sink)
+    o_fed, lse_fed = rf.round_to(o, out_dtype), rf.round_to(lse, "f32")
+    mdq = rf.emulate_dq_rows(qh, kh, vh, doh, o_fed, lse_fed, case.scale, case.is_causal, case.dtype, rows, bias=bias)
+    return {"o": o, "lse": lse, "o_model": o_pre, "o_fed": o_fed, "lse_fed": lse_fed, "dq": dq, "dq_model": mdq,
+            "out_dtype": out_dtype}
+
+
+def compare_rows(case, got, want):
+    """compare() for O, LSE and dQ of sampled rows (no dK/dV: those sum over every row)."""
+    tol = TOL["stated"][case.dtype]
+    odt = want["out_dtype"]
+    report = {}
+    for name in ("o", "dq"):
+        t = tol["fwd"] if name == "o" else tol["bwd"]
+        g, w, m = got[name], want[name], want[name + "_model"]
+        assert np.all(np.isfinite(g)), f"{name}: non-finite output"
+        floor = float(np.abs(m - w).max())
+        bound = t + floor + half_ulp(np.maximum(np.abs(g), np.abs(w)), odt)
+        report[name] = (float((np.abs(g - w) / bound).max()), 1.0, floor)
+    fin = np.isfinite(want["lse"])
+    assert np.array_equal(np.isneginf(got["lse"]), np.isneginf(want["lse"])), "lse: -inf rows differ"
+    report["lse"] = (float(np.abs(got["lse"][fin] - want["lse"][fin]).max()) if fin.any() else 0.0,
+                     TOL["lse"][case.dtype], 0.0)
+    bad = {k: v for k, v in report.items() if not v[0] <= v[1]}
+    assert not bad, f"{case.shape_str}: parity violated {bad} (all: {report})"
+    return report
 
 
 def slice_group(case, got, b, hk):

@@ -171,3 +171,90 @@ def test_mask_kind_none_ignores_the_mask_arguments():
     st = lib.sdpa_fwd_masked(p(1), p(1), p(1), p(1), p(0), 1, 2, 1, 16, 16, 80, 0.125, 1, 0, p(0), -5, -5, -5, p(0),
                              1, 1, p(0), 0, None)
     assert st == 3
+
+
+# ---- the Python binding checks every tensor before any call into the library -------------
+
+def _meta(shape, dtype=None):
+    import torch
+
+    names = {"f16": torch.float16, "f32": torch.float32, "bf16": torch.bfloat16, "u8": torch.uint8,
+             "bool": torch.bool}
+    return torch.empty(shape, dtype=names.get(dtype, dtype) if dtype is not None else torch.bfloat16, device="meta")
+
+
+@pytest.fixture
+def as_gpu(monkeypatch):
+    """Pose meta tensors (no memory behind them) as tensors on cuda:0, so that only the
+    shape, dtype and layout rules decide; a check that let one through would go on to ask
+    the library for a workspace size and then fail on the missing stream, never launching."""
+    import torch
+
+    monkeypatch.setattr(torch.Tensor, "device", property(lambda self: torch.device("cuda", 0)))
+
+
+B, HQ, HKV, LQ, LKV, D = 2, 4, 2, 16, 24, 64
+
+
+def _fwd_args():
+    return dict(q=_meta((B, HQ, LQ, D)), k=_meta((B, HKV, LKV, D)), v=_meta((B, HKV, LKV, D)),
+                out=_meta((B, HQ, LQ, D)), lse=_meta((B, HQ, LQ), "f32"))
+
+
+@pytest.mark.parametrize("change,match", [
+    (dict(k=_meta((B + 1, HKV, LKV, D)), v=_meta((B + 1, HKV, LKV, D))), "batch or head size"),
+    (dict(k=_meta((B, HKV, LKV, 32)), v=_meta((B, HKV, LKV, 32))), "batch or head size"),
+    (dict(v=_meta((B, HKV, LKV + 1, D))), "differ"),
+    (dict(k=_meta((B, HKV, LKV, D), "f16")), "dtypes differ"),
+    (dict(q=_meta((B, 3, LQ, D)), ), "not a multiple"),
+    (dict(out=_meta((B, HQ, LQ + 1, D))), "out has shape"),
+    (dict(out=_meta((B, HQ, LQ, D), "f32")), "out has dtype"),
+    (dict(lse=_meta((B, HQ, LQ), "bf16")), "lse has dtype"),
+    (dict(lse=_meta((B, HQ, LQ + 1), "f32")), "lse has shape"),
+    (dict(workspace=_meta((16,), "u8"), q=_meta((B, HQ, 4, D)), k=_meta((B, HKV, 8192, D)),
+          v=_meta((B, HKV, 8192, D)), out=_meta((B, HQ, 4, D)), lse=_meta((B, HQ, 4), "f32")), "workspace holds"),
+    (dict(attn_mask=_meta((B, 1, LQ, LKV + 1), "bool")), "does not broadcast"),
+    (dict(attn_mask=_meta((B, 1, LQ, LKV), "f16")), "attn_mask must be bool"),
+    (dict(sinks=_meta((HQ + 1,), "f32")), "sinks must be float32"),
+])
+def test_binding_forward_rejects_mismatched_tensors(as_gpu, change, match):
+    args = _fwd_args()
+    args.update(change)
+    q, k, v = args.pop("q"), args.pop("k"), args.pop("v")
+    with pytest.raises(ValueError, match=match):
+        sd.sdpa_fwd(q, k, v, **args)
+
+
+@pytest.mark.parametrize("which,shape,dt,match", [
+    ("o", (B, HQ, LQ, D + 1), None, "o has shape"),
+    ("o", (B, HQ, LQ, D), "f32", "o has dtype"),
+    ("lse", (B, HQ), "f32", "lse has shape"),
+    ("dO", (B, HQ, LQ, D), "f16", "dO has dtype"),
+    ("dO", (B, HQ, LQ - 1, D), None, "dO has shape"),
+    ("dq", (B, HQ, LQ, D), "f32", "dq has dtype"),
+    ("dk", (B, HQ, LKV, D), None, "dk has shape"),
+    ("dv", (B, HKV, LKV - 1, D), None, "dv has shape"),
+    ("workspace", (8,), "u8", "workspace holds"),
+])
+def test_binding_backward_rejects_mismatched_tensors(as_gpu, which, shape, dt, match):
+    import torch
+
+    dtypes = {None: torch.bfloat16, "f16": torch.float16, "f32": torch.float32, "u8": torch.uint8}
+    args = dict(o=_meta((B, HQ, LQ, D)), lse=_meta((B, HQ, LQ), torch.float32), dO=_meta((B, HQ, LQ, D)),
+                dq=_meta((B, HQ, LQ, D)), dk=_meta((B, HKV, LKV, D)), dv=_meta((B, HKV, LKV, D)))
+    args[which] = _meta(shape, dtypes[dt])
+    q, k, v = _meta((B, HQ, LQ, D)), _meta((B, HKV, LKV, D)), _meta((B, HKV, LKV, D))
+    o, lse, dO = args.pop("o"), args.pop("lse"), args.pop("dO")
+    with pytest.raises(ValueError, match=match):
+        sd.sdpa_bwd(q, k, v, o, lse, dO, **args)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    q = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU only"):
+        sd.sdpa_fwd(q, q, q)
+    with pytest.raises(ValueError, match="GPU only"):
+        sd.sdpa_bwd(q, q, q, q, torch.zeros((1, 2, 8)), q)
+

@@ -19,10 +19,13 @@ def _cpu(shape, dtype=torch.float32):
     return torch.zeros(shape, dtype=dtype)
 
 
-@pytest.mark.parametrize("shape,dtype", [((1, 2, 8, 64), torch.float32), ((1, 2, 8, 64), torch.float64), ((2, 8, 64), torch.float16)])
-def test_cpu_tensors_raise_before_any_call(shape, dtype):
-    # No CPU fallback: host tensors are refused before the library is touched.
-    with pytest.raises(ValueError, match="GPU only"):
+@pytest.mark.parametrize("shape,dtype,match", [((1, 2, 8, 64), torch.float32, "GPU only"),
+                                               ((1, 2, 8, 64), torch.float64, "dtype"),
+                                               ((2, 8, 64), torch.float16, r"\[B, H, L, D\]")])
+def test_cpu_tensors_raise_before_any_call(shape, dtype, match):
+    # No CPU fallback: host tensors are refused before the library is touched (an eligible
+    # one for its device, the others for their dtype or rank, which are checked first).
+    with pytest.raises(ValueError, match=match):
         sd.attention(_cpu(shape, dtype), _cpu(shape, dtype), _cpu(shape, dtype))
 
 

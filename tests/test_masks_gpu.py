@@ -80,8 +80,8 @@ def _inputs(c, seed):
 @pytest.mark.parametrize("case_def", CASES, ids=[_id(c) for c in CASES])
 def test_mask_and_sink_parity(case_def, device):
     case, mask, sk = _inputs(case_def, seed=5)
-    got = run_gpu(case, case.dtype, device, mask=mask, sinks=sk)
     want = reference(case, case.dtype, mask=mask, sinks=sk)
+    got = run_gpu(case, case.dtype, device, mask=mask, sinks=sk, fed=want)
     rep = compare(case, got, want)
     print(" ".join(f"{k}={v[0]:.2e}/{v[1]:.2e}" for k, v in rep.items()), flush=True)
     if mask is not None and case_def[10]:  # rows with no key: O = 0, LSE = -inf
@@ -92,8 +92,18 @@ def test_mask_and_sink_parity(case_def, device):
                          ids=[_id(c) for c in CASES if c[6] != "f32"][1::3])
 def test_mask_and_sink_parity_fp32_out(case_def, device):
     case, mask, sk = _inputs(case_def, seed=9)
-    got = run_gpu(case, "f32", device, mask=mask, sinks=sk)
-    compare(case, got, reference(case, "f32", mask=mask, sinks=sk))
+    want = reference(case, "f32", mask=mask, sinks=sk)
+    compare(case, run_gpu(case, "f32", device, mask=mask, sinks=sk, fed=want), want)
+
+
+@pytest.mark.parametrize("case_def", [c for c in CASES if c[6] != "f32"][2::4],
+                         ids=[_id(c) for c in CASES if c[6] != "f32"][2::4])
+def test_mask_and_sink_parity_end_to_end(case_def, device):
+    """The backward fed by the GPU forward's own O and LSE (the bound then allows R, the
+    spread that the forward output's rounding causes in Delta)."""
+    case, mask, sk = _inputs(case_def, seed=11)
+    want = reference(case, case.dtype, mask=mask, sinks=sk, end_to_end=True)
+    compare(case, run_gpu(case, case.dtype, device, mask=mask, sinks=sk), want)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -53,7 +53,7 @@ def test_repeated_keys_at_max_length(device, Lq):
            "dq": inp.from_torch(dq, "f32"), "dk": inp.from_torch(dkr[0], "f32")[None, None] * R,
            "dv": inp.from_torch(dvr[0], "f32")[None, None] * R}
     del dk, dv, dkr, dvr
-    rep = compare(case, got, reference(case, "f32"))
+    rep = compare(case, got, reference(case, "f32", end_to_end=True))
     print(" ".join(f"{n}={e:.2e}/{b:.2e}" for n, (e, b, _) in rep.items()), flush=True)
     assert np.all(np.isfinite(got["lse"]))
 
@@ -82,5 +82,5 @@ def test_repeated_queries_at_max_length(device):
            "dq": inp.from_torch(dq_r[:, :, 0], "f32"), "dk": inp.from_torch(dk, "f32") / R,
            "dv": inp.from_torch(dv, "f32") / R}
     del o, lse, dq, o_r, l_r, dq_r
-    rep = compare(case, got, reference(case, "f32"))
+    rep = compare(case, got, reference(case, "f32", end_to_end=True))
     print(" ".join(f"{n}={e:.2e}/{b:.2e}" for n, (e, b, _) in rep.items()), flush=True)

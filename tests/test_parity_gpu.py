@@ -85,16 +85,48 @@ def _id(c):
 @pytest.mark.parametrize("case_def", CASES, ids=[_id(c) for c in CASES])
 def test_parity_native_out(case_def, device):
     case = inp.make_case(*case_def, seed=0)
-    got = run_gpu(case, case.dtype, device)
-    compare(case, got, reference(case, case.dtype))
+    want = reference(case, case.dtype)
+    compare(case, run_gpu(case, case.dtype, device, fed=want), want)
 
 
 @pytest.mark.parametrize("case_def", [c for c in CASES if c[6] != "f32"][::2],
                          ids=[_id(c) for c in CASES if c[6] != "f32"][::2])
 def test_parity_fp32_out(case_def, device):
     case = inp.make_case(*case_def, seed=1)
-    got = run_gpu(case, "f32", device)
-    compare(case, got, reference(case, "f32"))
+    want = reference(case, "f32")
+    compare(case, run_gpu(case, "f32", device, fed=want), want)
+
+
+@pytest.mark.parametrize("case_def", CASES[1::3], ids=[_id(c) for c in CASES[1::3]])
+def test_parity_end_to_end(case_def, device):
+    """Forward then backward on the GPU's own O and LSE, as a training step runs: the bound
+    allows R, the spread that the rounding of the stored O causes in Delta_i."""
+    case = inp.make_case(*case_def, seed=2)
+    want = reference(case, case.dtype, end_to_end=True)
+    compare(case, run_gpu(case, case.dtype, device), want)
+
+
+# Scale of zero (every visible key weighs the same) and negative scales, on every path:
+# tiled causal and ragged, short-query causal and with split keys, float32.
+SCALE_CASES = [
+    (1, 4, 2, 150, 150, 64, "bf16", True),
+    (1, 2, 1, 70, 300, 128, "f16", False),
+    (1, 4, 2, 100, 260, 96, "bf16", True),
+    (2, 8, 2, 4, 1000, 64, "bf16", True),
+    (2, 16, 4, 8, 4099, 128, "f16", False),
+    (1, 4, 2, 37, 100, 64, "f32", True),
+]
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, -0.3])
+@pytest.mark.parametrize("case_def", SCALE_CASES, ids=[_id(c) for c in SCALE_CASES])
+def test_parity_zero_and_negative_scale(case_def, scale, device):
+    case = inp.make_case(*case_def, seed=6, scale=scale)
+    want = reference(case, case.dtype)
+    got = run_gpu(case, case.dtype, device, fed=want)
+    compare(case, got, want)
+    if scale == 0.0:  # uniform weights: the gradients of Q and K vanish
+        assert np.all(got["dq"] == 0) and np.all(got["dk"] == 0)
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
@@ -103,14 +135,14 @@ def test_large_logits_and_rising_scores(dt, device):
     moves in every tile; both stress the exp2-domain rescaling."""
     case = inp.make_case(1, 4, 2, 300, 300, 64, dt, is_causal=True, seed=3)
     case.q = inp.from_f32(inp.as_float64(case.q, dt).astype(np.float32) * 10.0, dt)
-    got = run_gpu(case, "f32", device)
-    compare(case, got, reference(case, "f32"))
+    want = reference(case, "f32")
+    compare(case, run_gpu(case, "f32", device, fed=want), want)
     case2 = inp.make_case(1, 2, 2, 64, 700, 64, dt, is_causal=False, seed=4)
     k = inp.as_float64(case2.k, dt)
     k *= np.linspace(0.2, 3.0, k.shape[2])[None, None, :, None]
     case2.k = inp.from_f32(k.astype(np.float32), dt)
-    got2 = run_gpu(case2, "f32", device)
-    compare(case2, got2, reference(case2, "f32"))
+    want2 = reference(case2, "f32")
+    compare(case2, run_gpu(case2, "f32", device, fed=want2), want2)
 
 
 @pytest.mark.parametrize("case_def", [(2, 8, 2, 200, 200, 64, "bf16", True), (2, 8, 2, 4, 3000, 128, "f16", False),

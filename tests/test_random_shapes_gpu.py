@@ -46,5 +46,5 @@ def _id(c):
 @pytest.mark.parametrize("case_def", CASES, ids=[_id(c) for c in CASES])
 def test_random_shape_parity(case_def, device):
     case = inp.make_case(*case_def, seed=7)
-    got = run_gpu(case, case.dtype, device)
-    compare(case, got, reference(case, case.dtype))
+    want = reference(case, case.dtype)
+    compare(case, run_gpu(case, case.dtype, device, fed=want), want)
