@@ -53,7 +53,8 @@
  *             accumulated into).
  * Scale       Any finite value, including 0 (every visible key weighs the same) and
  *             negative values; a non-finite scale is SDPA_ERR_VALUE.
- * Threads     No mutable global state; calls are thread-safe.
+ * Threads     No mutable global state (except the fixed scratch of
+ *             sdpa_bwd_noalloc, below); calls are thread-safe.
  */
 #ifndef SDPA_MI355X_H
 #define SDPA_MI355X_H
@@ -234,6 +235,27 @@ sdpa_status_t sdpa_bwd_masked_stage(int stage, const void* q, const void* k, con
                                     int64_t mask_stride_b, int64_t mask_stride_h, int64_t mask_stride_q,
                                     const float* sinks, float* dsinks, sdpa_dtype_t dtype, sdpa_dtype_t out_dtype,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, serving loops that must not call
+ * hipMalloc, harnesses that forbid it). The scratch that sdpa_bwd keeps in the
+ * caller's workspace lives instead in a fixed array of SDPA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library, one per GPU, held until the process ends. The call
+ * allocates and frees nothing. Arguments, results and errors are those of sdpa_bwd,
+ * plus SDPA_ERR_WORKSPACE when sdpa_workspace_bytes(1, ...) for these sizes exceeds
+ * the array (the bf16 GQA shape B=4, Hq=32, Hkv=4, L=4096, D=128 needs 4 MiB), and
+ * SDPA_ERR_DEVICE when the array's address cannot be obtained on the current device.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ * (nothing in it needs to start at zero): calls on one GPU that may overlap, on
+ * different streams or from different threads, race on it and must be ordered by the
+ * caller.
+ */
+#define SDPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+sdpa_status_t sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                               int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype,
+                               sdpa_dtype_t out_dtype, void* stream);
 
 /* Static string naming a status code. Never NULL. */
 const char* sdpa_status_str(sdpa_status_t status);

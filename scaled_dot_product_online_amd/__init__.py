@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     SdpaError,
     library,
     sdpa_bwd,
+    sdpa_bwd_noalloc,
     sdpa_fwd,
     select_path,
     status_str,

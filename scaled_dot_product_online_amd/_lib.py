@@ -20,7 +20,8 @@ PATH_TILED, PATH_VECTOR, PATH_FP32 = 0, 1, 2
 PATH_NAMES = {PATH_TILED: "tiled", PATH_VECTOR: "vector", PATH_FP32: "fp32"}
 MASK_NONE, MASK_BOOL, MASK_ADDITIVE = 0, 1, 2
 SYMBOLS = ("sdpa_select_path", "sdpa_workspace_bytes", "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_stage", "sdpa_fwd_masked",
-           "sdpa_bwd_masked", "sdpa_bwd_masked_stage", "sdpa_status_str")
+           "sdpa_bwd_masked", "sdpa_bwd_masked_stage", "sdpa_bwd_noalloc", "sdpa_status_str")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SDPA_NOALLOC_SCRATCH_BYTES in include/sdpa.h
 
 _lib = None
 
@@ -59,6 +60,8 @@ def library():
     lib.sdpa_bwd_masked.restype = c_int
     lib.sdpa_bwd_masked_stage.argtypes = [c_int] + lib.sdpa_bwd_masked.argtypes
     lib.sdpa_bwd_masked_stage.restype = c_int
+    lib.sdpa_bwd_noalloc.argtypes = lib.sdpa_bwd.argtypes[:19] + [vp]
+    lib.sdpa_bwd_noalloc.restype = c_int
     lib.sdpa_status_str.argtypes = [c_int]
     lib.sdpa_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -343,3 +346,30 @@ def sdpa_bwd(q, k, v, o, lse, dO, scale=None, is_causal=False, out_dtype=None, d
     _check(st)
     return dq, dk, dv, (dsinks if sk is not None else None)
 
+
+def sdpa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, scale=None, is_causal=False, stream=None):
+    """sdpa_bwd_noalloc: the backward into caller-provided dq, dk, dv (out dtype = their
+    dtype), with the library's fixed per-GPU scratch instead of a workspace. Allocates
+    nothing; calls that may overlap on one GPU race on the scratch (include/sdpa.h)."""
+    import torch
+
+    check_eligible(q, k, v, is_causal)
+    _contig(q, k, v)
+    B, Hq, Lq, D = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    dt = _torch_code(q.dtype)
+    odt = _torch_code(dq.dtype)
+    tdt = _torch_dtype(odt)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    check_buffer("o", o, (B, Hq, Lq, D), tdt, q.device)
+    check_buffer("lse", lse, (B, Hq, Lq), torch.float32, q.device)
+    check_buffer("dO", dO, (B, Hq, Lq, D), q.dtype, q.device)
+    check_buffer("dq", dq, (B, Hq, Lq, D), tdt, q.device)
+    check_buffer("dk", dk, (B, Hkv, Lkv, D), tdt, q.device)
+    check_buffer("dv", dv, (B, Hkv, Lkv, D), tdt, q.device)
+    st = library().sdpa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, Hq, Hkv, Lq, Lkv, D, scale, int(bool(is_causal)), dt, odt,
+                                    _stream(q.device, stream))
+    _check(st)
+    return dq, dk, dv

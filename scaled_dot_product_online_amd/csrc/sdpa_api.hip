@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/sdpa.h"
 #include "kernels.h"
 
@@ -265,6 +267,55 @@ sdpa_status_t sdpa_bwd_masked_stage(int stage, const void* q, const void* k, con
   return run_bwd(stage == 0 ? sdpa::kStage0 : sdpa::kStage1, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D,
                  scale, is_causal, mask_kind, mask, mask_stride_b, mask_stride_h, mask_stride_q, sinks, dsinks, dtype,
                  out_dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the backward without a workspace argument ------------------------------------------
+// The fixed scratch of sdpa_bwd_noalloc. In host code `scratch` names a host-side stand-in,
+// not device memory: the device address of each GPU's copy comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[SDPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, null until first looked up
+
+// Device address of the current device's scratch, or null on failure.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+sdpa_status_t sdpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                               int64_t Lq, int64_t Lkv, int64_t D, float scale, int is_causal, sdpa_dtype_t dtype,
+                               sdpa_dtype_t out_dtype, void* stream) {
+  // Sizes first (a pure host check), so that an oversized call fails before any device call.
+  sdpa_status_t st = check_shape(B, Hq, Hkv, Lq, Lkv, D, is_causal, dtype, out_dtype);
+  if (st != SDPA_OK) return st;
+  const size_t need = ws_bytes(1, Shape{B, Hq, Hkv, Lq, Lkv, D}, path_of(Hq, Hkv, Lq, is_causal, dtype),
+                               is_causal != 0);
+  if (need > SDPA_NOALLOC_SCRATCH_BYTES) return SDPA_ERR_WORKSPACE;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return SDPA_ERR_NULL;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return SDPA_ERR_DEVICE;
+  return run_bwd(sdpa::kStagesAll, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, Lq, Lkv, D, scale, is_causal,
+                 SDPA_MASK_NONE, nullptr, 0, 0, 0, nullptr, nullptr, dtype, out_dtype, ws,
+                 SDPA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 const char* sdpa_status_str(sdpa_status_t status) {

@@ -258,3 +258,16 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU only"):
         sd.sdpa_bwd(q, q, q, q, torch.zeros((1, 2, 8)), q)
 
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_before_any_device_call():
+    _no_device()
+    lib = sd.library()
+    p = lambda x: ctypes.c_void_p(x * 256 if x else 0)  # noqa: E731  (never dereferenced)
+    ptrs = [p(1)] * 9
+    # 2 x 64 x 16384 query rows of {LSE, Delta} pairs (8 bytes) = 16 MiB fits the 64 MiB scratch;
+    # with small-grid partials a tiny-grid shape can need more. 16 x 64 x 65536 rows: 512 MiB.
+    assert lib.sdpa_bwd_noalloc(*ptrs, 16, 64, 8, 65536, 65536, 128, 0.125, 1, 2, 2, None) == 4
+    assert lib.sdpa_bwd_noalloc(*ptrs, 0, 64, 8, 64, 64, 128, 0.125, 1, 2, 2, None) == 2  # shape checks first
+    ptrs[4] = p(0)
+    assert lib.sdpa_bwd_noalloc(*ptrs, 1, 8, 8, 64, 64, 64, 0.125, 0, 1, 1, None) == 1  # lse is required
+    assert sd.workspace_bytes(1, 16, 64, 8, 65536, 65536, 128, True, sd.BF16) > _lib.NOALLOC_SCRATCH_BYTES
