@@ -258,12 +258,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
     }
   };
 
-  const srd_t rk = make_srd(k + kvoff, (uint32_t)Lkv * D * 2);
-  const srd_t rv = make_srd(v + kvoff, (uint32_t)Lkv * D * 2);
+  const uint16_t* kbase = k + kvoff;
+  const uint16_t* vbase = v + kvoff;
+  const typename TL::template DmaPlan<kDqBN, 4> dma(wave, lane);
   if (t_lo < t_hi) {
     uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
-    TL::template dma_fill<kDqBN>(rk, b0, t_lo * kDqBN, wave, 4, lane);
-    TL::template dma_fill<kDqBN>(rv, b0 + TILE, t_lo * kDqBN, wave, 4, lane);
+    dma.fill(srd_rows<D>(kbase, Lkv, t_lo * kDqBN), b0, wave);
+    dma.fill(srd_rows<D>(vbase, Lkv, t_lo * kDqBN), b0 + TILE, wave);
   }
   // Key padding: tiles whose keys are all padding are skipped (mask bytes read a tile ahead).
   const bool pad = HAS_MASK && is_key_padding(mask);
@@ -273,8 +274,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
     __syncthreads();
     if (t + 1 < t_hi) {
       uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
-      TL::template dma_fill<kDqBN>(rk, nb, (t + 1) * kDqBN, wave, 4, lane);
-      TL::template dma_fill<kDqBN>(rv, nb + TILE, (t + 1) * kDqBN, wave, 4, lane);
+      dma.fill(srd_rows<D>(kbase, Lkv, (t + 1) * kDqBN), nb, wave);
+      dma.fill(srd_rows<D>(vbase, Lkv, (t + 1) * kDqBN), nb + TILE, wave);
     }
     const uint32_t kept = kept_next;
     if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * kDqBN, kDqBN, Lkv, lane);
@@ -401,13 +402,12 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   const int ft0 = TL::f(trow);
   const int tcol = 8 * (L16 & 1);  // byte within the 16-byte chunk
   const int tch = (L16 & 3) >> 1;  // chunk 2*db + tch
+  const typename TL::template DmaPlan<kKvBM, kKvWaves> dma(wave, lane);
   auto issue = [&](int it, uint8_t* buf) {
     const int gi = it % G, t0 = tile_of(it);
     const int64_t head = (int64_t)(b * Hq + hk * G + gi);
-    const srd_t rq = make_srd(q + head * Lq * D, (uint32_t)Lq * D * 2);
-    const srd_t rdo = make_srd(dO + head * Lq * D, (uint32_t)Lq * D * 2);
-    TL::template dma_fill<kKvBM>(rq, buf, t0, wave, kKvWaves, lane);
-    TL::template dma_fill<kKvBM>(rdo, buf + TILE, t0, wave, kKvWaves, lane);
+    dma.fill(srd_rows<D>(q + head * Lq * D, Lq, t0), buf, wave);
+    dma.fill(srd_rows<D>(dO + head * Lq * D, Lq, t0), buf + TILE, wave);
     if (wave == kKvWaves - 1 && lane < STAT / 16) {
       const srd_t rs = make_srd(rowstat + head * lq_pad + t0, (uint32_t)(Lq - t0) * 8);
       dma16(rs, buf + 2 * TILE, (uint32_t)(16 * lane));

@@ -278,7 +278,45 @@ struct SwzTile {
         dma16_untracked<CPOL>(src, lds + 1024 * j, off);
     }
   }
+  // The same copy for a kernel that fills many tiles: wave w of WAVES computes the
+  // source offsets of its slices once (they do not depend on the tile's first row), and
+  // each tile's first row goes into the buffer resource instead (srd_rows), so a tile
+  // costs no vector ALU work; rows past the tensor's end still arrive as zeros.
+  template <int ROWS, int WAVES>
+  struct DmaPlan {
+    static constexpr int SLICES = ROWS * CPR / 64;
+    static constexpr int NS = (SLICES + WAVES - 1) / WAVES;  // slices of one wave (at most)
+    static_assert(ROWS * CPR % 64 == 0, "tile must be a whole number of 1 KiB slices");
+    uint32_t off[NS];
+    __device__ __forceinline__ DmaPlan(int w, int lane) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int pc_lin = 64 * (w + s * WAVES) + lane;
+        const int r = pc_lin / CPR, pc = pc_lin % CPR;
+        off[s] = (uint32_t)((r * D + (pc ^ f(r)) * 8) * 2);
+      }
+    }
+    template <int CPOL = kCacheDefault, bool TRACKED = true>
+    __device__ __forceinline__ void fill(srd_t src, uint8_t* lds, int w) const {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int j = w + s * WAVES;
+        if (SLICES % WAVES != 0 && j >= SLICES) break;
+        if constexpr (TRACKED)
+          dma16<CPOL>(src, lds + 1024 * j, off[s]);
+        else
+          dma16_untracked<CPOL>(src, lds + 1024 * j, off[s]);
+      }
+    }
+  };
 };
+
+// Buffer resource of rows [g0, rows) of a row-major [rows, D] 16-bit tensor at `base`
+// (no records when g0 >= rows): a tile's copy with DmaPlan addresses its rows from here.
+template <int D>
+__device__ __forceinline__ srd_t srd_rows(const uint16_t* base, int rows, int g0) {
+  return make_srd(base + (int64_t)g0 * D, (uint32_t)max(0, rows - g0) * (uint32_t)(D * 2));
+}
 
 // ---- global ------------------------------------------------------------------------
 __device__ __forceinline__ u32x4_t gload16B(const void* p) { return *(const u32x4_t*)p; }

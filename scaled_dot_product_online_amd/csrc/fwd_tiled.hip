@@ -128,12 +128,13 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
   const int fv = TL::f(vrow), fv8 = TL::f(vrow + 8);  // swizzle of the two rows each transposed read pair uses
   const int vx = 2 * (G16 & 1) + ((L16 & 3) >> 1);
 
-  const srd_t rk = make_srd(k + kvoff, (uint32_t)Lkv * D * 2);
-  const srd_t rv = make_srd(v + kvoff, (uint32_t)Lkv * D * 2);
+  const uint16_t* kbase = k + kvoff;
+  const uint16_t* vbase = v + kvoff;
+  const typename TL::template DmaPlan<kFwdBN, 4> dma(wave, lane);
   if (t_lo < t_hi) {
     uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
-    TL::template dma_fill<kFwdBN>(rk, b0, t_lo * kFwdBN, wave, 4, lane);
-    TL::template dma_fill<kFwdBN>(rv, b0 + TILE, t_lo * kFwdBN, wave, 4, lane);
+    dma.fill(srd_rows<D>(kbase, Lkv, t_lo * kFwdBN), b0, wave);
+    dma.fill(srd_rows<D>(vbase, Lkv, t_lo * kFwdBN), b0 + TILE, wave);
   }
   // Key padding: a tile whose keys are all padding adds nothing and is skipped; its mask
   // bytes are read one tile ahead.
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     __syncthreads();  // tile t is in LDS; every wave has finished tile t - 1
     if (t + 1 < t_hi) {
       uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
-      TL::template dma_fill<kFwdBN>(rk, nb, (t + 1) * kFwdBN, wave, 4, lane);
-      TL::template dma_fill<kFwdBN>(rv, nb + TILE, (t + 1) * kFwdBN, wave, 4, lane);
+      dma.fill(srd_rows<D>(kbase, Lkv, (t + 1) * kFwdBN), nb, wave);
+      dma.fill(srd_rows<D>(vbase, Lkv, (t + 1) * kFwdBN), nb + TILE, wave);
     }
     const uint32_t kept = kept_next;
     if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * kFwdBN, kFwdBN, Lkv, lane);

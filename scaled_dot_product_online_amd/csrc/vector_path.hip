@@ -130,15 +130,16 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
   // step st + 2 as soon as S^T of step st has been read out of it, and the V slot as soon
   // as P V has: each tile is requested about two steps before it is used.
   uint8_t* my = lds + wave * WAVE_LDS;
-  const srd_t rk = make_srd(k + kv0 * D, (uint32_t)Lkv * D * 2);
-  const srd_t rv = make_srd(v + kv0 * D, (uint32_t)Lkv * D * 2);
+  const uint16_t* kbase = k + kv0 * D;
+  const uint16_t* vbase = v + kv0 * D;
   auto kslot = [&](int st) { return my + (st & 1) * 2 * TILE; };
   auto vslot = [&](int st) { return my + (st & 1) * 2 * TILE + TILE; };
+  const typename TL::template DmaPlan<kVecKeys, 1> dma(0, lane);
   auto fill_k = [&](int st) {
-    TL::template dma_fill<kVecKeys, kCacheStream, false>(rk, kslot(st), kb0 + st * kVecKeys, 0, 1, lane);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(kbase, Lkv, kb0 + st * kVecKeys), kslot(st), 0);
   };
   auto fill_v = [&](int st) {
-    TL::template dma_fill<kVecKeys, kCacheStream, false>(rv, vslot(st), kb0 + st * kVecKeys, 0, 1, lane);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(vbase, Lkv, kb0 + st * kVecKeys), vslot(st), 0);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -456,12 +457,13 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
   const int kb1 = min(kb0 + seg, Lkv);
   const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
   uint8_t* my = lds + wave * WAVE_LDS;
-  const srd_t rk = make_srd(k + kv0 * D, (uint32_t)Lkv * D * 2);
-  const srd_t rv = make_srd(v + kv0 * D, (uint32_t)Lkv * D * 2);
+  const uint16_t* kbase = k + kv0 * D;
+  const uint16_t* vbase = v + kv0 * D;
+  const typename TL::template DmaPlan<kVecKeys, 1> dma(0, lane);
   auto fill = [&](int st) {
     uint8_t* slot = my + (st % kVecRing) * 2 * TILE;
-    TL::template dma_fill<kVecKeys, kCacheStream, false>(rk, slot, kb0 + st * kVecKeys, 0, 1, lane);
-    TL::template dma_fill<kVecKeys, kCacheStream, false>(rv, slot + TILE, kb0 + st * kVecKeys, 0, 1, lane);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(kbase, Lkv, kb0 + st * kVecKeys), slot, 0);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(vbase, Lkv, kb0 + st * kVecKeys), slot + TILE, 0);
   };
 
   // LDS geometry (as in the tiled forward): 16-byte reads of row n, chunk 2c + g; transposed
