@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libsdpa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["sdpa_api.hip", "fwd_tiled.hip", "bwd_tiled.hip", "vector_path.hip", "fp32_path.hip", "delta.hip"]
+SOURCES = ["sdpa_api.hip", "fwd_tiled.hip", "bwd_tiled.hip", "vector_path.hip", "fp32_path.hip", "sink_grad.hip"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]

@@ -11,7 +11,7 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO.
 //
 // Kernel 1 (dq_kernel): one workgroup = 4 waves x 32 query rows of one (b, hq).
-//   It first forms Delta for its rows from O and dO and stores {LSE*log2e, Delta}
+//   It first forms Delta for its rows from O and dO and stores {LSE*log2e, -Delta}
 //   per query in the workspace for kernel 2, then streams K/V tiles of 64 keys
 //   through double-buffered, swizzled LDS filled by direct buffer-to-LDS loads. Like the forward it works on
 //   transposed scores (S^T = K Q^T, dP^T = V dO^T) so that each lane owns one
@@ -63,7 +63,7 @@ __device__ __forceinline__ void load_out8<f16_t>(rsrc_t r, uint32_t elem, float*
 }
 
 // ---------------------------------------------------------------------------------
-// Stage 0: dQ, plus the per-query {LSE*log2e, Delta} pairs for stage 1
+// Stage 0: dQ, plus the per-query {LSE*log2e, -Delta} pairs for stage 1
 // ---------------------------------------------------------------------------------
 constexpr int kDqBM = 128;  // query rows per workgroup
 // Keys per tile: 64, or 32 at D = 256, where the resident Q/dO operands and the dQ
@@ -133,7 +133,8 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
   if (HAS_MASK && lse2 == -INFINITY) lse2 = INFINITY;
   const int64_t mrow =
       HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
-  if (row_ok && g == 0 && split == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, dlt};
+  // -Delta: the dK/dV kernel starts its dP accumulators from it.
+  if (row_ok && g == 0 && split == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, -dlt};
 
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
             const int i = 8 * c2 + e;
             float nb = -lse2;
             if constexpr (HAS_MASK) nb = bias[e] - lse2;
-            float p = fast_exp2(fminf(fmaf(s[i], scale_log2, nb), 0.f));
+            float p = exp2_le1(fmaf(s[i], scale_log2, nb));
             if constexpr (EDGE)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
               p = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) < klim ? p : 0.f;
             ds[e] = p * (dp[i] - dlt);
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   constexpr int kKvWaves = kv_waves<D>();
   constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
   constexpr int TILE = kKvBM * TL::RB;
-  constexpr int STAT = kKvBM * 8;       // {LSE*log2e, Delta} of the tile's queries
+  constexpr int STAT = kKvBM * 8;       // {LSE*log2e, -Delta} of the tile's queries
   constexpr int BUF = 2 * TILE + STAT;  // one buffer: Q tile, dO tile, stats
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
 
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int qm = 0; qm < 4; ++qm) {
       s[qm] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      dp[qm] = (f32x4_t){-sa[qm][1], -sa[qm][3], -sb[qm][1], -sb[qm][3]};
+      dp[qm] = (f32x4_t){sa[qm][1], sa[qm][3], sb[qm][1], sb[qm][3]};
     }
     u32x2_t tb[2][8];
 #pragma unroll
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
                 nb += mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh + (int64_t)qi * mask.sq);
               }
             }
-            float p = fast_exp2(fminf(fmaf(s[qm][j], scale_log2, nb), 0.f));
+            float p = exp2_le1(fmaf(s[qm][j], scale_log2, nb));
             if constexpr (EDGE) {  // query t0 + qm*16 + j + 4*q4 exists and, if causal, sees key krow
               const int u = t0 + qm * 16 + j + co;  // wave-uniform part
               p = (q4x4 < Lq + co - u && (!CAUSAL || q4x4 - krow >= -u)) ? p : 0.f;
@@ -613,7 +614,7 @@ int dkv_splits(const Shape& s, bool causal) {
                      (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM));
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-// Workspace: {LSE*log2e, Delta} pairs, then (split grids) the dQ partials, then the dK and
+// Workspace: {LSE*log2e, -Delta} pairs, then (split grids) the dQ partials, then the dK and
 // dV partials.
 size_t rowstat_bytes(const Shape& s) { return align256((size_t)(s.B * s.Hq * tiled_rowstat_stride(s.Lq)) * 8); }
 size_t dq_part_bytes(const Shape& s) {
@@ -629,7 +630,7 @@ template <typename T, int D, bool C, bool M, typename OutT>
 hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q, const void* k, const void* v,
                         const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, float* ws,
                         float scale, int stages, hipStream_t st) {
-  f32x2_t* rowstat = (f32x2_t*)ws;  // [B*Hq][lq_pad] {LSE*log2e, Delta}
+  f32x2_t* rowstat = (f32x2_t*)ws;  // [B*Hq][lq_pad] {LSE*log2e, -Delta}
   const int lq_pad = (int)tiled_rowstat_stride(s.Lq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int G = (int)(s.Hq / s.Hkv);

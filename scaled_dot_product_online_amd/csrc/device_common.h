@@ -84,6 +84,10 @@ template <typename T> __device__ __forceinline__ float hi_f32(uint32_t w) { retu
 // ---- exp2 / log2 (hardware v_exp_f32 / v_log_f32) --------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+// exp2(min(x, 0)): the backward's probabilities with the exponent clamped above at 0, as
+// exp2(x) clamped to [0, 1] (equal, since exp2 is increasing and exp2(0) = 1), which the
+// compiler folds into the clamp bit of v_exp_f32 instead of a separate v_min_f32.
+__device__ __forceinline__ float exp2_le1(float x) { return __builtin_amdgcn_fmed3f(fast_exp2(x), 0.f, 1.f); }
 
 // ---- half-wave exchange: lanes l and l^32 ------------------------------------------
 // v_permlane32_swap exchanges the upper half of its first operand with the

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(const float* __rest
       const float dp = row_sum<R>(dot_slice<D>(dov, v_lds, j, slice));
       const int key = t0 + j;
       const float nb = HAS_MASK && key < Lkv ? mask_bias_log2<float>(mask.p, mask.kind, mrow + key) - lse2 : -lse2;
-      float p = fast_exp2(fminf(fmaf(sv, scale_log2, nb), 0.f));
+      float p = exp2_le1(fmaf(sv, scale_log2, nb));
       if (key >= Lkv || (CAUSAL && key > qrow + co)) p = 0.f;
       const float ds = p * (dp - dlt);
       const float* kr = k_lds + j * TL::PITCH + slice * TL::SP;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kF32Threads) void dkv_f32_kernel(const float* __res
           nb += mask_bias_log2<float>(mask.p, mask.kind,
                                       (int64_t)b * mask.sb + (int64_t)hq * mask.sh +
                                           (int64_t)min(i, Lq - 1) * mask.sq + min(krow, Lkv - 1));
-        float p = fast_exp2(fminf(fmaf(sv, scale_log2, nb), 0.f));
+        float p = exp2_le1(fmaf(sv, scale_log2, nb));
         if (i >= Lq || (CAUSAL && krow > i + co)) p = 0.f;
         const float ds = p * (dp - dl_lds[j]);
         const float* qr = q_lds + j * TL::PITCH + slice * TL::SP;

@@ -44,9 +44,10 @@ __device__ __forceinline__ uint32_t key_kept(const Mask& mask, int b, int key0, 
   return (lane < n && key < Lkv) ? ((const uint8_t*)mask.p)[(int64_t)b * mask.sb + key] : 0u;
 }
 
-// dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * Delta(b,h,i), with Delta(b,h,i) at
-// delta[((b*Hq + h) * pitch + i) * es] (delta.hip). One deterministic reduction per head.
-hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es,
+// dsinks[h] = -sum_{b,i} exp(sinks[h] - lse[b,h,i]) * Delta(b,h,i), where dsign * Delta(b,h,i)
+// sits at delta[((b*Hq + h) * pitch + i) * es] (sink_grad.hip). One deterministic reduction
+// per head.
+hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es, float dsign,
                             const float* sinks, float* dsinks, hipStream_t st);
 
 
@@ -62,7 +63,7 @@ hipError_t launch_fwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Ma
 
 // Tiled backward, 16-bit operands (bwd_tiled.hip). `ws` is the workspace of
 // tiled_bwd_workspace(s, causal) bytes: first, per (b, hq), a row of tiled_rowstat_stride(Lq)
-// {LSE*log2e, Delta} fp32 pairs; then, on small grids, fp32 partials of dQ and of dK, dV.
+// {LSE*log2e, -Delta} fp32 pairs; then, on small grids, fp32 partials of dQ and of dK, dV.
 inline int64_t tiled_rowstat_stride(int64_t Lq) { return (Lq + 63) / 64 * 64; }
 size_t tiled_bwd_workspace(const Shape& s, bool causal);
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,

@@ -65,7 +65,7 @@ size_t ws_bytes(int backward, const Shape& s, int path, bool causal) {
     return 0;
   }
   // The vector backward forms Delta inside its kernel; the fp32 path keeps Delta and the
-  // tiled path {LSE*log2e, Delta} pairs per query row in the workspace.
+  // tiled path {LSE*log2e, -Delta} pairs per query row in the workspace.
   if (path == SDPA_PATH_VECTOR) return align_up(sdpa::vector_bwd_workspace(s));
   if (path == SDPA_PATH_TILED) return align_up(sdpa::tiled_bwd_workspace(s, causal));  // + split partials, small grids
   return delta_bytes(s);
@@ -195,10 +195,11 @@ sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, c
   const bool causal = is_causal != 0;
   float* delta = (float*)workspace;
   hipError_t e;
-  // Where stage 0 leaves Delta_i for the sinks' gradient: element (bh * pitch + i) * es.
+  // Where stage 0 leaves Delta_i (times dsign) for the sinks' gradient: element (bh * pitch + i) * es.
   const float* dl;
   int64_t pitch;
   int es;
+  float dsign = 1.f;
   switch (path) {
     case SDPA_PATH_FP32:
       e = sdpa::launch_bwd_f32(s, causal, mask, (const float*)q, (const float*)k, (const float*)v, (const float*)o,
@@ -213,11 +214,11 @@ sdpa_status_t run_bwd(int stages, const void* q, const void* k, const void* v, c
     default:
       e = sdpa::launch_bwd_tiled(s, (sdpa::Dt)dtype, (sdpa::Dt)out_dtype, causal, mask, q, k, v, o, lse, dO, dq, dk,
                                  dv, delta, scale, stages, hs);
-      dl = delta + 1, pitch = sdpa::tiled_rowstat_stride(Lq), es = 2;  // {LSE*log2e, Delta} pairs
+      dl = delta + 1, pitch = sdpa::tiled_rowstat_stride(Lq), es = 2, dsign = -1.f;  // {LSE*log2e, -Delta} pairs
       break;
   }
   if (e == hipSuccess && sinks && (stages & sdpa::kStage1))
-    e = sdpa::launch_sink_grad(s, lse, dl, pitch, es, sinks, dsinks, hs);
+    e = sdpa::launch_sink_grad(s, lse, dl, pitch, es, dsign, sinks, dsinks, hs);
   return device_status(e);
 }
 

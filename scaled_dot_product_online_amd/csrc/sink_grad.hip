@@ -19,7 +19,7 @@ constexpr int kDeltaThreads = 256;
 // order: the result does not depend on scheduling.
 __global__ __launch_bounds__(kDeltaThreads) void sink_grad_kernel(const float* __restrict__ lse,
                                                                   const float* __restrict__ delta, int64_t pitch,
-                                                                  int es, const float* __restrict__ sinks,
+                                                                  int es, float dsign, const float* __restrict__ sinks,
                                                                   float* __restrict__ dsinks, int B, int Hq, int Lq) {
   const int h = blockIdx.x;
   const float sk = sinks[h];
@@ -40,16 +40,16 @@ __global__ __launch_bounds__(kDeltaThreads) void sink_grad_kernel(const float* _
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < kDeltaThreads / 64; ++w) t += part[w];
-    dsinks[h] = -t;
+    dsinks[h] = -dsign * t;  // the stored values are dsign * Delta
   }
 }
 
 }  // namespace
 
-hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es,
+hipError_t launch_sink_grad(const Shape& s, const float* lse, const float* delta, int64_t pitch, int es, float dsign,
                             const float* sinks, float* dsinks, hipStream_t st) {
-  hipLaunchKernelGGL(sink_grad_kernel, dim3((unsigned)s.Hq), dim3(kDeltaThreads), 0, st, lse, delta, pitch, es, sinks,
-                     dsinks, (int)s.B, (int)s.Hq, (int)s.Lq);
+  hipLaunchKernelGGL(sink_grad_kernel, dim3((unsigned)s.Hq), dim3(kDeltaThreads), 0, st, lse, delta, pitch, es, dsign,
+                     sinks, dsinks, (int)s.B, (int)s.Hq, (int)s.Lq);
   return hipGetLastError();
 }
 

@@ -550,7 +550,7 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
                                           (int64_t)(r % Lq) * mask.sq + min(key, Lkv - 1));
             }
           }
-          float p = fast_exp2(fminf(fmaf(s[i], scale_log2, nb), 0.f));
+          float p = exp2_le1(fmaf(s[i], scale_log2, nb));
           if (r0 + j >= rows || key >= kb1 || (CAUSAL && key > lim4[j])) p = 0.f;
           pv[4 * h + j] = p;
           dsv[4 * h + j] = p * (dp[i] - d4[j]);

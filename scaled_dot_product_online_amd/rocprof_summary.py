@@ -1,7 +1,7 @@
 """Summarise rocprofv3 CSV output into the short text files kept under profiles/.
 
     python -m scaled_dot_product_online_amd.rocprof_summary --name NAME --command "CMD" \
-        --trace DIR [--fetch DIR --write DIR --calib-bytes N]
+        [--trace DIR] [--fetch DIR --write DIR --calib-bytes N] [--sq DIR [DIR ...]]
 
 --trace    directory of a `rocprofv3 --kernel-trace --stats --output-format csv` run
 --fetch    directory of a `rocprofv3 --pmc FETCH_SIZE` run of the same program
@@ -12,11 +12,26 @@
 --bench-log    stdout of the traced bench.py run: its own HIP-event times per stage (timed
            steps only; the trace's averages also hold the warm-up calls) are listed beside
            the durations.
+--sq       directories of `rocprofv3 --pmc` runs of the same program with SQ (shader
+           sequencer) and GRBM counters, at most 8 SQ counters per run; their per-dispatch
+           means are merged by kernel name into one table of instruction mix, matrix-core
+           occupancy, waits and the shader clock (counters.json keeps the raw means).
 
-Writes profiles/NAME.md (per-kernel durations, and per-dispatch HBM traffic when
-counter runs are given) and, for the traffic, profiles/NAME.traffic.json keyed by
-the sha256 of the HIP sources, so that bench.py reports `traffic` only for the
-kernel build the counters were taken on.
+Writes profiles/NAME.md (per-kernel durations, and per-dispatch HBM traffic and
+instruction counters when those runs are given) and, for the traffic and the counters,
+profiles/NAME.traffic.json and profiles/NAME.counters.json keyed by the sha256 of the HIP
+sources, so that bench.py reports `traffic` only for the kernel build the counters were
+taken on.
+
+Counter arithmetic (MI355X: 256 CUs of 4 SIMDs in 8 XCDs, each XCD with its own GRBM):
+  clock           GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (dispatch timestamps of the
+                  same run)
+  matrix busy     SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8): the share
+                  of SIMD cycles in which the matrix core works (the busy count equals the
+                  instructions' issue cycles: 32 per 32x32x16, 16 per 16x16x32 16-bit MFMA)
+  per MFMA        SQ_INSTS_{VALU - MFMA, LDS, SALU} / SQ_INSTS_MFMA (SQ_INSTS_VALU counts
+                  the MFMA instructions too)
+  waits           SQ_WAIT_INST_LDS, SQ_WAIT_ANY, SQ_WAIT_INST_ANY as shares of SQ_WAVE_CYCLES
 """
 
 from __future__ import annotations
@@ -62,22 +77,65 @@ def counter_means(d):
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
 
+def sq_means(dirs):
+    """{kernel: {counter: mean per dispatch}} over several --pmc runs, with each run's mean
+    dispatch duration in ns as duration_ns@<run> (for the clock of that run's GRBM counts)."""
+    out = collections.defaultdict(dict)
+    for run, d in enumerate(dirs):
+        vals = collections.defaultdict(lambda: collections.defaultdict(list))
+        durs = collections.defaultdict(dict)
+        for r in read_csv(d, "counter_collection.csv"):
+            k = short(r["Kernel_Name"])
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            durs[k][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for k, cs in vals.items():
+            for c, v in cs.items():
+                out[k][c if c not in out[k] else f"{c}@{run}"] = sum(v) / len(v)
+                if c == "GRBM_GUI_ACTIVE":
+                    out[k][f"duration_ns@{run}"] = sum(durs[k].values()) / len(durs[k])
+                    out[k][f"GRBM_GUI_ACTIVE@{run}"] = sum(v) / len(v)
+    return out
+
+
+def sq_derived(c):
+    """Derived per-kernel figures from the merged SQ / GRBM means (None where a counter is missing)."""
+    g = lambda n: c.get(n)  # noqa: E731
+    clocks = [c[k] / 8.0 / c["duration_ns@" + k.split("@")[1]] for k in c
+              if k.startswith("GRBM_GUI_ACTIVE@") and c.get("duration_ns@" + k.split("@")[1])]
+    cycles = g("GRBM_GUI_ACTIVE") / 8.0 if g("GRBM_GUI_ACTIVE") else None
+    mfma = g("SQ_INSTS_MFMA")
+    d = {"clock_GHz": sum(clocks) / len(clocks) if clocks else None}
+    d["mfma_busy"] = (g("SQ_VALU_MFMA_BUSY_CYCLES") / (1024.0 * cycles)
+                      if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None and cycles else None)
+    if mfma:
+        d["valu_per_mfma"] = (g("SQ_INSTS_VALU") - mfma) / mfma if g("SQ_INSTS_VALU") is not None else None
+        d["lds_per_mfma"] = g("SQ_INSTS_LDS") / mfma if g("SQ_INSTS_LDS") is not None else None
+        d["salu_per_mfma"] = g("SQ_INSTS_SALU") / mfma if g("SQ_INSTS_SALU") is not None else None
+    wc = g("SQ_WAVE_CYCLES")
+    for n, key in (("SQ_WAIT_INST_LDS", "wait_lds"), ("SQ_WAIT_ANY", "wait_any"), ("SQ_WAIT_INST_ANY", "wait_issue")):
+        d[key] = g(n) / wc if wc and g(n) is not None else None
+    d["lds_bank_conflict_cycles"] = g("SQ_LDS_BANK_CONFLICT")
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--name", required=True)
     ap.add_argument("--command", required=True)
-    ap.add_argument("--trace", required=True)
+    ap.add_argument("--trace")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--calib-bytes", type=int, default=0)
     ap.add_argument("--bench-log")
+    ap.add_argument("--sq", nargs="+")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args()
 
-    stats = read_csv(a.trace, "kernel_stats.csv")
-    lines = [f"# {a.name}", "", "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", "",
-             "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
-             "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    stats = read_csv(a.trace, "kernel_stats.csv") if a.trace else []
+    lines = [f"# {a.name}", "", "Command (run from the repository root on one MI355X):", "", "```", a.command, "```", ""]
+    if stats:
+        lines += ["## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
+                  "| kernel | calls | average us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
@@ -114,12 +172,34 @@ def main():
             rd, wr = fetch[k] * f_scale * 1024, write.get(k, 0.0) * w_scale * 1024
             lines.append(f"| `{short(k)}` | {fetch[k]:.0f} | {write.get(k, 0.0):.0f} | {rd:.4g} | {wr:.4g} |")
             traffic["kernels"][short(k)] = {"read_bytes": rd, "write_bytes": wr}
+    counters = None
+    if a.sq:
+        merged = sq_means(a.sq)
+        fmt = lambda x, f: "—" if x is None else format(x, f)  # noqa: E731
+        lines += ["", "## Instruction counters per dispatch (rocprofv3 --pmc, SQ and GRBM blocks)", "",
+                  "| kernel | clock GHz | matrix busy | VALU / MFMA | LDS / MFMA | SALU / MFMA | waiting on LDS | "
+                  "waiting (s_waitcnt) | waiting to issue | LDS bank-conflict cycles |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
+        counters = {"source_sha256": sources_sha256(), "kernels": {}}
+        for k in sorted(merged):
+            dv = sq_derived(merged[k])
+            if not merged[k].get("SQ_INSTS_MFMA") and not merged[k].get("SQ_INSTS_VALU"):
+                continue
+            lines.append(f"| `{k}` | {fmt(dv['clock_GHz'], '.2f')} | {fmt(dv['mfma_busy'], '.1%')} | "
+                         f"{fmt(dv.get('valu_per_mfma'), '.2f')} | {fmt(dv.get('lds_per_mfma'), '.2f')} | "
+                         f"{fmt(dv.get('salu_per_mfma'), '.2f')} | {fmt(dv['wait_lds'], '.1%')} | "
+                         f"{fmt(dv['wait_any'], '.1%')} | {fmt(dv['wait_issue'], '.1%')} | "
+                         f"{fmt(dv['lds_bank_conflict_cycles'], '.3g')} |")
+            counters["kernels"][k] = {"means": merged[k], "derived": dv}
     os.makedirs(a.out, exist_ok=True)
     with open(os.path.join(a.out, f"{a.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     if traffic is not None:
         with open(os.path.join(a.out, f"{a.name}.traffic.json"), "w") as f:
             json.dump(traffic, f, indent=1)
+    if counters is not None:
+        with open(os.path.join(a.out, f"{a.name}.counters.json"), "w") as f:
+            json.dump(counters, f, indent=1)
     print("\n".join(lines))
 
 
