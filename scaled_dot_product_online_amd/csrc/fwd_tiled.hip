@@ -162,14 +162,25 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    // K operands are read 2 stage(s) of the contraction ahead of the matrix-core
+    // instructions that use them, behind scheduling fences.
+    constexpr int KD = 2 + 1;
+    u32x4_t ka[KD][kFwdBN / 32];
+    auto load_k = [&](int c, u32x4_t* a) {
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
+      for (int kb = 0; kb < kFwdBN / 32; ++kb)
+        a[kb] = *(const u32x4_t*)(kt + (kb * 32 + n) * TL::RB + ((2 * c + g) ^ fk) * 16);
+    };
 #pragma unroll
-      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
-        const int ch = 2 * c + g;
-        const u32x4_t a = *(const u32x4_t*)(kt + (kb * 32 + n) * TL::RB + (ch ^ fk) * 16);
-        s[kb] = mfma32<T>(a, qop[c], s[kb]);
-      }
+    for (int c = 0; c < KD - 1; ++c) load_k(c, ka[c]);
+    sched_fence();
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      if (c + KD - 1 < D / 16) load_k(c + KD - 1, ka[(c + KD - 1) % KD]);
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) s[kb] = mfma32<T>(ka[c % KD][kb], qop[c], s[kb]);
+      sched_fence();
+    }
 
     if constexpr (MASKED) {  // every tile: s <- s*scale*log2e + bias, keys past the end -inf
 #pragma unroll
