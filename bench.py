@@ -27,6 +27,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -59,7 +61,7 @@ def parse():
 class Runner:
     """Device buffers for one workload and a step() that runs fwd + bwd stage 0 + stage 1."""
 
-    def __init__(self, name, device):
+    def __init__(self, name, device, rotate=False):
         import torch
 
         import scaled_dot_product_online_amd as sd
@@ -70,6 +72,11 @@ class Runner:
         self.case = inp.make_case(B, Hq, Hkv, Lq, Lkv, D, dt, is_causal=causal, seed=0)
         c = self.case
         self.q, self.k, self.v, self.do = (inp.to_torch(getattr(c, n), dt, device) for n in ("q", "k", "v", "do"))
+        # rotate: two copies of K and V used in turn, so that no call finds the other's
+        # operands in the 256 MB memory-side cache (short-query shapes whose K and V are
+        # about that size).
+        self.kv = [(self.k, self.v)] + ([(self.k.clone(), self.v.clone())] if rotate else [])
+        self.turn = 0
         mask, sinks = mask_and_sinks(name)
         self.mask = None if mask is None else torch.from_numpy(mask[1]).to(device)
         self.sinks = None if sinks is None else torch.from_numpy(sinks).to(device)
@@ -97,12 +104,15 @@ class Runner:
         self.bwd_bytes = (qb + 2 * kb + qb + qb + lse_b) + (qb + 2 * kb)
 
     def fwd(self):
-        self.sd.sdpa_fwd(self.q, self.k, self.v, scale=self.case.scale, is_causal=self.case.is_causal, out=self.o,
+        self.turn = (self.turn + 1) % len(self.kv)
+        k, v = self.kv[self.turn]
+        self.sd.sdpa_fwd(self.q, k, v, scale=self.case.scale, is_causal=self.case.is_causal, out=self.o,
                          lse=self.lse, workspace=self.ws_f, stream=self.stream, attn_mask=self.mask,
                          sinks=self.sinks)
 
     def bwd(self, stage):
-        self.sd.sdpa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, scale=self.case.scale,
+        k, v = self.kv[self.turn]
+        self.sd.sdpa_bwd(self.q, k, v, self.o, self.lse, self.do, scale=self.case.scale,
                          is_causal=self.case.is_causal, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_b,
                          stream=self.stream, stage=stage, attn_mask=self.mask, sinks=self.sinks, dsinks=self.dsinks)
 
@@ -134,38 +144,66 @@ class Runner:
         return wall, ms
 
 
-def cpu_baseline(case, budget_s=10.0):
-    """fp64 oracle, fwd+bwd, on whole GQA groups of the same inputs, timed on host cores.
+def blas_info():
+    """(threads, library and version) of the BLAS that NumPy calls, after loading it."""
+    import numpy as np
 
-    Groups (b, hk) are taken in order until ~budget_s seconds of CPU work or all are done."""
-    from oracle import sdpa_reference as ref
-
+    np.ones((64, 64)) @ np.ones((64, 64))
     try:
         import threadpoolctl
 
-        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return int(info[0].get("num_threads", 1)), f"{info[0].get('internal_api')} {info[0].get('version')}"
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        pass
+    return len(os.sched_getaffinity(0)), "unknown"
+
+
+def cpu_baseline(case, budget_s=10.0, mask=None, sinks=None):
+    """fp64 oracle on whole GQA groups of the same inputs, timed on host cores.
+
+    Each group (b, hk) runs the forward alone, then forward + backward (the backward
+    recomputes the forward), in order until ~budget_s seconds of CPU work (at least one
+    group). Reports fwd+bwd TFLOP/s, and the mean seconds per group of both."""
+    from oracle import sdpa_reference as ref
+
+    threads, blas = blas_info()
     G = case.Hq // case.Hkv
     groups = [(b, hk) for b in range(case.B) for hk in range(case.Hkv)]
-    done, elapsed = 0, 0.0
+    om = None
+    if mask is not None:
+        om = np.asarray(mask[1], dtype=bool) if mask[0] == "bool" else inp.as_float64(mask[1], case.dtype)
+    done, t_fwd, t_all = 0, 0.0, 0.0
     for b, hk in groups:
-        q = case.f64("q")[b:b + 1, hk * G:(hk + 1) * G]
+        hs = slice(hk * G, (hk + 1) * G)
+        q = case.f64("q")[b:b + 1, hs]
         k = case.f64("k")[b:b + 1, hk:hk + 1]
         v = case.f64("v")[b:b + 1, hk:hk + 1]
-        do = case.f64("do")[b:b + 1, hk * G:(hk + 1) * G]
+        do = case.f64("do")[b:b + 1, hs]
+        m = None
+        if om is not None:
+            m4 = om.reshape((1,) * (4 - om.ndim) + om.shape)
+            m = m4[(slice(b, b + 1) if m4.shape[0] > 1 else slice(0, 1)), (hs if m4.shape[1] > 1 else slice(0, 1))]
+        sk = None if sinks is None else np.asarray(sinks, dtype=np.float64)[hs]
         t0 = time.perf_counter()
-        ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0)
-        elapsed += time.perf_counter() - t0
+        ref.attention_forward(q, k, v, case.scale, case.is_causal, mask=m, sinks=sk)
+        t1 = time.perf_counter()
+        ref.group_backward(q, k, v, do, case.scale, case.is_causal, 0, 0, mask=m, sinks=sk)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_all += t2 - t1
         done += 1
-        if elapsed >= budget_s:
+        if t_fwd + t_all >= budget_s:
             break
     f = done * (flops(1, G, case.Lq, case.Lkv, case.D, case.is_causal)
                 + flops(1, G, case.Lq, case.Lkv, case.D, case.is_causal, backward=True))
-    return {"value": f / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle fwd+bwd of {done} of {len(groups)} GQA groups ({G} query heads each, "
-                      f"L={case.Lq}, D={case.D}, causal={case.is_causal}) of the same workload; {elapsed:.1f} s of "
-                      f"CPU work; FLOPs counted as for the GPU"}
+    return {"value": f / t_all / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "fwd_s_per_group": t_fwd / done, "fwdbwd_s_per_group": t_all / done, "groups": done,
+            "groups_total": len(groups), "blas": blas,
+            "sample": f"fp64 numpy oracle of {done} of {len(groups)} GQA groups ({G} query heads each, Lq={case.Lq}, "
+                      f"Lkv={case.Lkv}, D={case.D}, causal={case.is_causal}) of the same workload: forward alone, then "
+                      f"forward+backward ({t_all:.1f} s); value = fwd+bwd FLOPs counted as for the GPU / fwd+bwd time"}
 
 
 def measure(runner, steps, warmup):
@@ -278,7 +316,7 @@ def main():
         del src, dst
     names = [w[0] for w in WORKLOADS] if args.sweep else [args.workload]
     for name in names:
-        r = Runner(name, device)
+        r = Runner(name, device, rotate=args.sweep and BY_NAME[name][4] <= 8)
         m = measure(r, args.steps, args.warmup)
         line = {"metric": METRIC, "value": m["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True,
@@ -287,10 +325,13 @@ def main():
                 "bwd_tflops": m["bwd_tflops"], "fwd_frac_of_peak": m["fwd_frac_of_peak"],
                 "fwdbwd_frac_of_peak": m["fwdbwd_frac_of_peak"], "kernel_ms": m["kernel_ms"],
                 "roofline": m["roofline"]}
-        if not args.sweep:
-            if not args.no_vector:
-                line["vector_path"] = vector_line(device, args.steps, args.warmup)
-            line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(r.case)
+        if not args.sweep and not args.no_vector:
+            line["vector_path"] = vector_line(device, args.steps, args.warmup)
+        if args.sweep:
+            line["kv_copies"] = len(r.kv)
+        mask, sinks = mask_and_sinks(name)
+        line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(
+            r.case, budget_s=2.0 if args.sweep else 10.0, mask=mask, sinks=sinks)
         print(json.dumps(line), flush=True)
         del r
         torch.cuda.empty_cache()

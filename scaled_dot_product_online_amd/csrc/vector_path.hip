@@ -120,11 +120,14 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
     const int r = min(rb * 32 + n, rows - 1);
     mrow = (int64_t)b * mask.sb + (int64_t)(hk * G + r / Lq) * mask.sh + (int64_t)(r % Lq) * mask.sq;
   }
-  // This wave's contiguous key segment [kb0, kb1).
-  const int seg = split_len / kWaves;
-  const int kb0 = split * split_len + wave * seg;
-  const int kb1 = min(kb0 + seg, Lkv);
-  const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
+  // This wave's key tiles: the split's 32-key tiles [s0, kb1) taken round-robin by the
+  // waves, so that a workgroup's waves stream adjacent tiles (one front in HBM per
+  // workgroup rather than one per wave).
+  const int s0 = split * split_len;
+  const int kb1 = min(s0 + split_len, Lkv);
+  const int ntile = kb1 > s0 ? (kb1 - s0 + kVecKeys - 1) / kVecKeys : 0;
+  const int steps = ntile > wave ? (ntile - wave + kWaves - 1) / kWaves : 0;
+  auto tile0 = [&](int st) { return s0 + (st * kWaves + wave) * kVecKeys; };
 
   // Ring of 2 K slots and 2 V slots per wave. The K slot of step st is refilled with
   // step st + 2 as soon as S^T of step st has been read out of it, and the V slot as soon
@@ -136,10 +139,10 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
   auto vslot = [&](int st) { return my + (st & 1) * 2 * TILE + TILE; };
   const typename TL::template DmaPlan<kVecKeys, 1> dma(0, lane);
   auto fill_k = [&](int st) {
-    dma.template fill<kCacheStream, false>(srd_rows<D>(kbase, Lkv, kb0 + st * kVecKeys), kslot(st), 0);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(kbase, Lkv, tile0(st)), kslot(st), 0);
   };
   auto fill_v = [&](int st) {
-    dma.template fill<kCacheStream, false>(srd_rows<D>(vbase, Lkv, kb0 + st * kVecKeys), vslot(st), 0);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(vbase, Lkv, tile0(st)), vslot(st), 0);
   };
 
   const int G16 = lane >> 4, L16 = lane & 15;
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_fwd_kernel(const u
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint8_t* kt = kslot(st);
     const uint8_t* vt = vslot(st);
-    const int t0 = kb0 + st * kVecKeys;
+    const int t0 = tile0(st);
 
     // S^T = K Q^T: lane holds keys t0 + 8*(i/4) + 4g + i%4 of packed row n.
     f32x16_t s;
@@ -452,18 +455,20 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
   const uint8_t* qt = qd_lds;
   const uint8_t* dt = qd_lds + TILE;
 
-  const int seg = split_len / kWaves;
-  const int kb0 = split * split_len + wave * seg;
-  const int kb1 = min(kb0 + seg, Lkv);
-  const int steps = kb1 > kb0 ? (kb1 - kb0 + kVecKeys - 1) / kVecKeys : 0;
+  // Key tiles taken round-robin by the waves, as in the forward.
+  const int s0 = split * split_len;
+  const int kb1 = min(s0 + split_len, Lkv);
+  const int ntile = kb1 > s0 ? (kb1 - s0 + kVecKeys - 1) / kVecKeys : 0;
+  const int steps = ntile > wave ? (ntile - wave + kWaves - 1) / kWaves : 0;
+  auto tile0 = [&](int st) { return s0 + (st * kWaves + wave) * kVecKeys; };
   uint8_t* my = lds + wave * WAVE_LDS;
   const uint16_t* kbase = k + kv0 * D;
   const uint16_t* vbase = v + kv0 * D;
   const typename TL::template DmaPlan<kVecKeys, 1> dma(0, lane);
   auto fill = [&](int st) {
     uint8_t* slot = my + (st % kVecRing) * 2 * TILE;
-    dma.template fill<kCacheStream, false>(srd_rows<D>(kbase, Lkv, kb0 + st * kVecKeys), slot, 0);
-    dma.template fill<kCacheStream, false>(srd_rows<D>(vbase, Lkv, kb0 + st * kVecKeys), slot + TILE, 0);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(kbase, Lkv, tile0(st)), slot, 0);
+    dma.template fill<kCacheStream, false>(srd_rows<D>(vbase, Lkv, tile0(st)), slot + TILE, 0);
   };
 
   // LDS geometry (as in the tiled forward): 16-byte reads of row n, chunk 2c + g; transposed
@@ -499,7 +504,7 @@ __global__ __launch_bounds__(64 * vec_waves<D>(), 1) void vec_bwd_kernel(const u
     const uint8_t* kt = my + (st % kVecRing) * 2 * TILE;
     const uint8_t* vt = kt + TILE;
     uint16_t* dsw = kTight ? (uint16_t*)const_cast<uint8_t*>(vt) : ds_lds[wave];  // V is consumed once dP is formed
-    const int t0 = kb0 + st * kVecKeys;
+    const int t0 = tile0(st);
     const int key = t0 + n;  // this lane's key column
     // A mask that varies only along keys (query and head strides 0) has one bias per lane.
     float kbias = 0.f;
