@@ -184,8 +184,13 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
     for (int kb = 0; kb < NKB; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T for keys kb*32 .. +31 (lane owns query qrow and 16
       // of the keys).
-      u32x4_t kv[2][2];
-      load_s(kb, 0, kv[0]);
+      // K/V operands read SD - 1 stages ahead: two at D = 256 (one wave per SIMD, so the
+      // wave's own reads must cover the LDS latency; measured 6% faster there), one else
+      // (two stages ahead measured no faster with two waves per SIMD).
+      constexpr int SD = D == 256 ? 3 : 2;
+      u32x4_t kv[SD][2];
+#pragma unroll
+      for (int c = 0; c < SD - 1; ++c) load_s(kb, c, kv[c]);
       sched_fence();
       f32x16_t s, dp;
 #pragma unroll
@@ -196,10 +201,10 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
       u32x2_t tb[2][D / 16];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) load_s(kb, c + 1, kv[(c + 1) & 1]);
-        else load_q(kb, 0, tb[0]);
-        s = mfma32<T>(kv[c & 1][0], qop[c], s);
-        dp = mfma32<T>(kv[c & 1][1], doop[c], dp);
+        if (c + SD - 1 < NC) load_s(kb, c + SD - 1, kv[(c + SD - 1) % SD]);
+        else if (c + SD - 1 == NC) load_q(kb, 0, tb[0]);
+        s = mfma32<T>(kv[c % SD][0], qop[c], s);
+        dp = mfma32<T>(kv[c % SD][1], doop[c], dp);
         sched_fence();
       }
       // dS^T as B operands, one per 16-key half c2. Only the softmax is duplicated for
