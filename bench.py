@@ -258,6 +258,8 @@ def measured_traffic(runner, label):
     from scaled_dot_product_online_amd.rocprof_summary import sources_sha256
 
     sym = kernel_symbol(runner, label)
+    if sym is None:
+        return None
     sha = sources_sha256()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.json"))):
         with open(path) as f:

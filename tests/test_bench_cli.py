@@ -65,3 +65,10 @@ def test_more_than_one_gpu_is_refused(n):
                          text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_traffic_lookup_without_a_kernel_name(monkeypatch):
+    # The fp32 path has no kernel name in the lookup: no traffic, and no error, even when a
+    # summary of the current sources exists.
+    monkeypatch.setattr(bench, "kernel_symbol", lambda r, label: None)
+    assert bench.measured_traffic(_Runner("fp32", "f32", False, 64), "fwd") is None
