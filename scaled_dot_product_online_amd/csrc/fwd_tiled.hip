@@ -42,14 +42,17 @@ namespace {
 constexpr int kFwdBM = 128;  // query rows per workgroup
 constexpr int kFwdThreads = 256;
 // Keys per tile: 64, or 32 at D = 256, where the O accumulators alone take 128 registers
-// per lane and a 64-key score block would not fit beside them.
+// per lane and a 64-key score block would not fit beside them. Every head dim runs two
+// waves per SIMD (two workgroups per CU): at D = 256 that leaves 256 registers per lane
+// for 128 of accumulators and 64 of Q operands, and a few values kept for the epilogue
+// spill outside the key loop (measured 16-29% faster than one wave per SIMD).
 template <int D>
 constexpr int fwd_bn() {
   return D == 256 ? 32 : 64;
 }
 
 template <typename T, int D, bool CAUSAL, bool MASKED, typename OutT>
-__global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kernel(
+__global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     OutT* __restrict__ o, float* __restrict__ lse, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
     float scale_log2, Mask mask, const float* __restrict__ sinks, int nsplit, int split_tiles,
@@ -156,20 +159,29 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
     if (CAUSAL && kt0 > q0 + 31 + co) continue;  // tile entirely above this wave's diagonal
     if (pad && !__any(kept != 0u)) continue;  // every key of the tile is padding
 
+    // At D = 256 (two waves per SIMD, 128 registers of O accumulators) the lane constants
+    // of the LDS addresses are made opaque per tile, so that the compiler rebuilds each
+    // stage's address inside the loop instead of keeping all 16 live across it.
+    int fkx = fk, fvx = fv, fv8x = fv8, nrow = n * TL::RB;
+    if constexpr (D == 256) asm volatile("" : "+v"(fkx), "+v"(fvx), "+v"(fv8x), "+v"(nrow));
     // S^T = K Q^T: 32 keys x 32 queries per accumulator block.
     f32x16_t s[kFwdBN / 32];
 #pragma unroll
     for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-    // K operands are read 2 stage(s) of the contraction ahead of the matrix-core
-    // instructions that use them, behind scheduling fences.
-    constexpr int KD = 2 + 1;
+    // K operands are read KD - 1 stages of the contraction ahead of the matrix-core
+    // instructions that use them (two, or one at D = 256 for registers), behind
+    // scheduling fences.
+    constexpr int KD = D == 256 ? 2 : 3;
     u32x4_t ka[KD][kFwdBN / 32];
+    // Chunk 2c + g of row n sits at chunk (2c + g) ^ f(n); f < 16, so for c >= 8 (D = 256)
+    // that is 16 + ((2(c - 8) + g) ^ f(n)): eight lane-dependent offsets and constants.
+    static_assert(D / 16 <= 16, "chunk index split assumes at most 32 chunks per row");
     auto load_k = [&](int c, u32x4_t* a) {
 #pragma unroll
       for (int kb = 0; kb < kFwdBN / 32; ++kb)
-        a[kb] = *(const u32x4_t*)(kt + (kb * 32 + n) * TL::RB + ((2 * c + g) ^ fk) * 16);
+        a[kb] = *(const u32x4_t*)(kt + kb * 32 * TL::RB + nrow + ((2 * (c & 7) + g) ^ fkx) * 16 + (c >> 3) * 256);
     };
 #pragma unroll
     for (int c = 0; c < KD - 1; ++c) load_k(c, ka[c]);
@@ -255,8 +267,8 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const int ch = 4 * db + vx;
-          const u32x2_t lo = lds_read_tr16((const uint16_t*)(vrow_p + (ch ^ fv) * 16));
-          const u32x2_t hi = lds_read_tr16((const uint16_t*)(vrow_p + 8 * TL::RB + (ch ^ fv8) * 16));
+          const u32x2_t lo = lds_read_tr16((const uint16_t*)(vrow_p + (ch ^ fvx) * 16));
+          const u32x2_t hi = lds_read_tr16((const uint16_t*)(vrow_p + 8 * TL::RB + (ch ^ fv8x) * 16));
           oacc[db] = mfma32<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, pop, oacc[db]);
         }
       }
@@ -264,30 +276,34 @@ __global__ __launch_bounds__(kFwdThreads, D == 256 ? 1 : 2) void fwd_tiled_kerne
   }
 
   const float l = half_swap_sum(lsum);
+  // The epilogue's lane indices, rebuilt here from the lane count of the (full) execution
+  // mask rather than kept in registers across the key loop (at D = 256 they would spill).
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ge = lane_e >> 5, qre = q0 + (lane_e & 31);
   if (part_o != nullptr) {  // one key split: unnormalised partials [split][b*Hq*Lq + hq*Lq + q]
-    if (qrow < Lq) {
-      const int64_t prow = ((int64_t)split * n_bh + bh) * Lq + qrow;
+    if (qre < Lq) {
+      const int64_t prow = ((int64_t)split * n_bh + bh) * Lq + qre;
       float* po = part_o + prow * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          *(f32x4_t*)(po + db * 32 + 8 * r4 + 4 * g) =
+          *(f32x4_t*)(po + db * 32 + 8 * r4 + 4 * ge) =
               (f32x4_t){oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2], oacc[db][4 * r4 + 3]};
-      if (g == 0) *(f32x2_t*)(part_ml + prow * 2) = (f32x2_t){m, l};
+      if (ge == 0) *(f32x2_t*)(part_ml + prow * 2) = (f32x2_t){m, l};
     }
     return;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (qrow < Lq) {
-    OutT* orow = o + ((int64_t)bh * Lq + qrow) * D;
+  if (qre < Lq) {
+    OutT* orow = o + ((int64_t)bh * Lq + qre) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        Store4<OutT>::run(orow + db * 32 + 8 * r4 + 4 * g, oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv,
+        Store4<OutT>::run(orow + db * 32 + 8 * r4 + 4 * ge, oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv,
                           oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
-    if (lse != nullptr && g == 0) lse[(int64_t)bh * Lq + qrow] = (m + fast_log2(l)) * kLn2;
+    if (lse != nullptr && ge == 0) lse[(int64_t)bh * Lq + qre] = (m + fast_log2(l)) * kLn2;
   }
 }
 
