@@ -16,6 +16,8 @@
 //   through double-buffered, swizzled LDS filled by direct buffer-to-LDS loads. Like the forward it works on
 //   transposed scores (S^T = K Q^T, dP^T = V dO^T) so that each lane owns one
 //   query row; dQ^T += K^T dS^T reads K^T with the LDS transpose read.
+//   At D = 256 stage 0 runs dq16_kernel instead: 8 waves x 16 query rows on 16x16x32
+//   tiles and 32-key tiles, which fits two waves per SIMD.
 // Kernel 2 (dkv_kernel): one workgroup = 8 waves x 16 key rows of one (b, hk);
 //   the waves keep K and V of their rows in registers and accumulate dK and dV
 //   while streaming Q/dO tiles of 64 queries of every query head of the group.
@@ -66,15 +68,16 @@ __device__ __forceinline__ void load_out8<f16_t>(rsrc_t r, uint32_t elem, float*
 // Stage 0: dQ, plus the per-query {LSE*log2e, -Delta} pairs for stage 1
 // ---------------------------------------------------------------------------------
 constexpr int kDqBM = 128;  // query rows per workgroup
-// Keys per tile: 64, or 32 at D = 256, where the resident Q/dO operands and the dQ
-// accumulators take 384 registers per lane (one wave per SIMD).
+// Keys per tile: 64, or 32 at D = 256 (dq16_kernel below; 32-row waves there would hold
+// 256 registers of resident Q/dO operands and dQ accumulators, one wave per SIMD).
 template <int D>
 constexpr int dq_bn() {
   return D == 256 ? 32 : 64;
 }
 
+// D <= 128 (D = 256 runs dq16_kernel).
 template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
-__global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, const OutT* __restrict__ o,
                                                          const float* __restrict__ lse,
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
                                                          int Lkv, int n_qblk, int n_bh, int lq_pad,
                                                          float scale_log2, float scale, Mask mask, int nsplit,
                                                          int split_tiles, float* __restrict__ dq_part) {
+  static_assert(D <= 128, "D = 256 runs dq16_kernel");
   using TL = SwzTile<D>;
   constexpr int kDqBN = dq_bn<D>();
   constexpr int TILE = kDqBN * TL::RB;
@@ -184,10 +188,9 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
     for (int kb = 0; kb < NKB; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T for keys kb*32 .. +31 (lane owns query qrow and 16
       // of the keys).
-      // K/V operands read SD - 1 stages ahead: two at D = 256 (one wave per SIMD, so the
-      // wave's own reads must cover the LDS latency; measured 6% faster there), one else
-      // (two stages ahead measured no faster with two waves per SIMD).
-      constexpr int SD = D == 256 ? 3 : 2;
+      // K/V operands read SD - 1 = 1 stage ahead (two stages ahead measured no faster with
+      // two waves per SIMD).
+      constexpr int SD = 2;
       u32x4_t kv[SD][2];
 #pragma unroll
       for (int c = 0; c < SD - 1; ++c) load_s(kb, c, kv[c]);
@@ -312,6 +315,235 @@ __global__ __launch_bounds__(kThreads, D == 256 ? 1 : 2) void dq_kernel(const ui
       for (int r4 = 0; r4 < 4; ++r4)
         Store4<OutT>::run(out + db * 32 + 8 * r4 + 4 * g, acc[db][4 * r4] * scale, acc[db][4 * r4 + 1] * scale,
                           acc[db][4 * r4 + 2] * scale, acc[db][4 * r4 + 3] * scale);
+  }
+}
+
+// Stage 0 at D = 256 on 16-row waves: one workgroup = 8 waves x 16 query rows of one
+// (b, hq), 16x16x32 matrix-core tiles, 32-key K/V tiles. The resident Q^T/dO^T operands
+// (64 registers) and dQ^T accumulators (64) then leave room for two waves per SIMD, where
+// the 32-row kernel's 256 registers of operands and accumulators allow one; each wave reads
+// the whole K/V tile for 16 rows instead of 32 (twice the LDS reads per FLOP). Orientation
+// as the dK/dV kernel's: S^T = K Q^T puts four keys of one query in each lane, which is the
+// B-operand layout of dQ^T += K^T dS^T; K^T comes from the LDS transpose read.
+constexpr int kDq16Waves = 8;
+template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
+__global__ __launch_bounds__(64 * kDq16Waves, 1) void dq16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const OutT* __restrict__ o, const float* __restrict__ lse, const uint16_t* __restrict__ dO,
+    OutT* __restrict__ dq, f32x2_t* __restrict__ rowstat, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
+    int lq_pad, float scale_log2, float scale, Mask mask, int nsplit, int split_tiles, float* __restrict__ dq_part) {
+  static_assert(kDq16Waves * 16 == kDqBM, "8 waves of 16 rows make the 128-row query block");
+  using TL = SwzTile<D, 16>;
+  constexpr int BN = 32;  // keys per tile: two 16-key blocks
+  constexpr int TILE = BN * TL::RB;
+  constexpr int NC = D / 32;  // 32-wide steps of the S / dP contraction over d
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];  // [buffer][K, V]
+
+  // Work id: query block major, then key split, then (b, hq) (as the 32-row kernel).
+  const int wid = xcd_remap(blockIdx.x, n_qblk * n_bh * nsplit, G);
+  int qblk = wid / (n_bh * nsplit);
+  const int rest = wid - qblk * (n_bh * nsplit);
+  const int split = rest / n_bh;
+  const int bh = rest - split * n_bh;
+  if (CAUSAL) qblk = n_qblk - 1 - qblk;
+  const int b = bh / Hq, hq = bh - b * Hq;
+  const int hk = hq / G, Hkv = Hq / G;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int q0 = qblk * kDqBM + wave * 16;  // wave-uniform
+  const int qrow = q0 + n16;
+
+  const int64_t kvoff = (int64_t)(b * Hkv + hk) * Lkv * D;
+  const int64_t qoff = (int64_t)bh * Lq * D;
+  const rsrc_t rq = make_rsrc(q + qoff, (uint32_t)Lq * D * 2);
+  const rsrc_t rdo = make_rsrc(dO + qoff, (uint32_t)Lq * D * 2);
+  const rsrc_t ro = make_rsrc(o + qoff, (uint32_t)Lq * D * (uint32_t)sizeof(OutT));
+
+  // Q^T and dO^T B operands: lane (n16, q4) holds row qrow, d = 32c + 8*q4 .. +7. Delta from
+  // the stored O over this lane's quarter of the row, then summed over the four lanes.
+  u32x4_t qop[NC], doop[NC];
+  float dpart = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t e = (uint32_t)(qrow * D + 32 * c + 8 * q4);
+    qop[c] = buf_load16(rq, e * 2);
+    doop[c] = buf_load16(rdo, e * 2);
+    float ov[8];
+    load_out8<OutT>(ro, e, ov);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dpart = fmaf(lo_f32<T>(doop[c][w]), ov[2 * w], dpart);
+      dpart = fmaf(hi_f32<T>(doop[c][w]), ov[2 * w + 1], dpart);
+    }
+  }
+  dpart += __shfl_xor(dpart, 16);
+  const float dlt = dpart + __shfl_xor(dpart, 32);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    settle(qop[c]);
+    settle(doop[c]);
+  }
+  const bool row_ok = qrow < Lq;
+  float lse2 = row_ok ? lse[(int64_t)bh * Lq + qrow] * kLog2e : 0.f;
+  // A masked row that sees no key (LSE = -inf) has P = 0: +inf makes every exponent -inf.
+  if (HAS_MASK && lse2 == -INFINITY) lse2 = INFINITY;
+  const int64_t mrow =
+      HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
+  // -Delta: the dK/dV kernel starts its dP accumulators from it.
+  if (row_ok && q4 == 0 && split == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, -dlt};
+
+  // dQ^T block db: lane (n16, q4) holds d = 16*db + 4*q4 + i of query qrow.
+  f32x4_t acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
+
+  const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
+  const int kv_end = CAUSAL ? min(Lkv, qblk * kDqBM + kDqBM + co) : Lkv;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int t_lo = split * split_tiles, t_hi = min(ntiles, t_lo + split_tiles);  // this split's key tiles
+  const int key_lim = CAUSAL ? min(Lkv, qrow + 1 + co) : Lkv;
+  const int L16 = lane & 15;
+  const int fa0 = TL::f(n16);            // 16-byte reads: row kb*16 + n16 (f depends on the row mod 8)
+  const int trow = 4 * q4 + (L16 >> 2);  // transposed reads: rows trow and trow + 16
+  const int ft0 = TL::f(trow);
+  const int tcol = 8 * (L16 & 1);  // byte within the 16-byte chunk
+  const int tch = (L16 & 3) >> 1;  // chunk 2*db + tch
+
+  // One key tile. Stage c of the S / dP products reads its K/V operands one stage ahead.
+  // Chunk indices past 15 (d >= 128) keep bit 4 under the XOR with f < 16, so each address
+  // is a lane term plus a constant.
+  auto tile = [&](bool masked, const uint8_t* kt, const uint8_t* vt, int kt0) {
+    // Lane constants made opaque per tile, so that the compiler rebuilds the LDS addresses
+    // derived from them inside the loop instead of keeping each one live across it.
+    int fa = fa0, ft = ft0, srow = n16 * TL::RB, trow_b = trow * TL::RB + tcol, q4x = q4, tchx = tch,
+        klim = key_lim - 4 * q4;
+    asm volatile("" : "+v"(fa), "+v"(ft), "+v"(srow), "+v"(trow_b), "+v"(q4x), "+v"(tchx), "+v"(klim));
+    auto load_s = [&](int c, u32x4_t* kv) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int off = kb * 16 * TL::RB + srow + ((4 * (c & 3) + q4x) ^ fa) * 16 + (c >> 2) * 256;
+        kv[2 * kb] = *(const u32x4_t*)(kt + off);
+        kv[2 * kb + 1] = *(const u32x4_t*)(vt + off);
+      }
+    };
+    // dQ A operands of d block db: K^T rows (keys) 4*q4 + 0..3 and 16 + 4*q4 + 0..3.
+    auto load_q = [&](int db, u32x2_t* tb) {
+      const int off = trow_b + ((2 * (db & 7) + tchx) ^ ft) * 16 + (db >> 3) * 256;
+      tb[0] = lds_read_tr16((const uint16_t*)(kt + off));
+      tb[1] = lds_read_tr16((const uint16_t*)(kt + off + 16 * TL::RB));
+    };
+    u32x4_t kv[2][4];
+    load_s(0, kv[0]);
+    sched_fence();
+    f32x4_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[kb][i] = 0.f;
+        dp[kb][i] = 0.f;
+      }
+    u32x2_t tb[2][2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c + 1 < NC) load_s(c + 1, kv[(c + 1) & 1]);
+      else load_q(0, tb[0]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma16<T>(kv[c & 1][2 * kb], qop[c], s[kb]);
+        dp[kb] = mfma16<T>(kv[c & 1][2 * kb + 1], doop[c], dp[kb]);
+      }
+      sched_fence();
+    }
+    // dS^T as the B operand: keys 4*q4 + 0..3 (block 0) then 16 + 4*q4 + 0..3 (block 1).
+    u32x4_t dsop;
+    auto softmax = [&](auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
+      float ds[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float bias[4];
+        if constexpr (HAS_MASK) {
+          const int key0 = kt0 + kb * 16 + 4 * q4;
+          if (mask.vec4 && key0 < Lkv) {
+            mask_bias4_log2<T>(mask.p, mask.kind, mrow + key0, bias);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              bias[j] = key0 + j < Lkv ? mask_bias_log2<T>(mask.p, mask.kind, mrow + key0 + j) : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float nb = -lse2;
+          if constexpr (HAS_MASK) nb = bias[j] - lse2;
+          float p = exp2_le1(fmaf(s[kb][j], scale_log2, nb));
+          if constexpr (EDGE)  // key kt0 + kb*16 + 4*q4 + j below key_lim
+            p = kt0 + kb * 16 + j < klim ? p : 0.f;
+          ds[4 * kb + j] = p * (dp[kb][j] - dlt);
+        }
+      }
+      dsop = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
+    };
+    if (masked)
+      softmax(std::true_type{});
+    else
+      softmax(std::false_type{});
+    sched_fence();
+    // dQ^T += K^T dS^T, one 16-wide d block per step, reads one step ahead.
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      if (db + 1 < D / 16) load_q(db + 1, tb[(db + 1) & 1]);
+      const u32x2_t lo = tb[db & 1][0], hi = tb[db & 1][1];
+      acc[db] = mfma16<T>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, dsop, acc[db]);
+      sched_fence();
+    }
+  };
+
+  const uint16_t* kbase = k + kvoff;
+  const uint16_t* vbase = v + kvoff;
+  const typename TL::template DmaPlan<BN, kDq16Waves> dma(wave, lane);
+  if (t_lo < t_hi) {
+    uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
+    dma.fill(srd_rows<D>(kbase, Lkv, t_lo * BN), b0, wave);
+    dma.fill(srd_rows<D>(vbase, Lkv, t_lo * BN), b0 + TILE, wave);
+  }
+  // Key padding: tiles whose keys are all padding are skipped (mask bytes read a tile ahead).
+  const bool pad = HAS_MASK && is_key_padding(mask);
+  uint32_t kept_next = pad && t_lo < t_hi ? key_kept(mask, b, t_lo * BN, BN, Lkv, lane) : 1u;
+  for (int t = t_lo; t < t_hi; ++t) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < t_hi) {
+      uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
+      dma.fill(srd_rows<D>(kbase, Lkv, (t + 1) * BN), nb, wave);
+      dma.fill(srd_rows<D>(vbase, Lkv, (t + 1) * BN), nb + TILE, wave);
+    }
+    const uint32_t kept = kept_next;
+    if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * BN, BN, Lkv, lane);
+    const uint8_t* kt = lds + (t & 1) * 2 * TILE;
+    const uint8_t* vt = kt + TILE;
+    const int kt0 = t * BN;
+    if (CAUSAL && kt0 > q0 + 15 + co) continue;  // tile entirely above this wave's diagonal
+    if (pad && !__any(kept != 0u)) continue;     // every key of the tile is padding
+    tile((kt0 + BN > Lkv) || (CAUSAL && kt0 + BN - 1 > q0 + co), kt, vt, kt0);  // wave-uniform flag
+  }
+  if (dq_part != nullptr) {  // one key split: fp32 partial of dQ / scale, [split][b*Hq*Lq + hq*Lq + q]
+    if (row_ok) {
+      float* po = dq_part + (((int64_t)split * n_bh + bh) * Lq + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) *(f32x4_t*)(po + db * 16 + 4 * q4) = acc[db];
+    }
+    return;
+  }
+  if (row_ok) {
+    OutT* out = dq + qoff + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      Store4<OutT>::run(out + db * 16 + 4 * q4, acc[db][0] * scale, acc[db][1] * scale, acc[db][2] * scale,
+                        acc[db][3] * scale);
   }
 }
 
@@ -647,10 +879,16 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q,
     constexpr int BN = dq_bn<D>();
     const int nt = (int)((s.Lkv + BN - 1) / BN);
     float* dq_part = nsplit > 1 ? (float*)parts : nullptr;
-    hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kThreads), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
-                       (const uint16_t*)dO, (OutT*)dq, rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh,
-                       lq_pad, scale_log2, scale, mask, nsplit, (nt + nsplit - 1) / nsplit, dq_part);
+    if constexpr (D == 256)
+      hipLaunchKernelGGL((dq16_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(64 * kDq16Waves), 0,
+                         st, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
+                         (const uint16_t*)dO, (OutT*)dq, rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh,
+                         lq_pad, scale_log2, scale, mask, nsplit, (nt + nsplit - 1) / nsplit, dq_part);
+    else
+      hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kThreads), 0, st,
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
+                         (const uint16_t*)dO, (OutT*)dq, rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh,
+                         lq_pad, scale_log2, scale, mask, nsplit, (nt + nsplit - 1) / nsplit, dq_part);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && nsplit > 1) e = launch_split_reduce(s, out, nsplit, dq_part, dq, s.B * s.Hq * s.Lq, scale, st);
     if (e != hipSuccess) return e;

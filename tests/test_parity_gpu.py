@@ -67,13 +67,16 @@ for _dt in ("f16", "bf16"):
         # backward splits on small grids: dK/dV over its (query head, query tile) sequence
         (1, 8, 1, 512, 256, 64, _dt, False),    # 16 splits, GQA 8:1
         (1, 4, 1, 256, 200, 256, _dt, False),   # 4 splits, head dim 256 (4-wave workgroups)
-        # head dim 256 (32-key forward / dQ tiles, 4-wave dK/dV, 2-wave short-query kernels)
+        # head dim 256 (32-key forward / dQ tiles, 16-row dQ waves, 4-wave dK/dV, 2-wave short-query kernels)
         (1, 4, 2, 200, 200, 256, _dt, True),    # tiled, causal
         (1, 4, 1, 70, 300, 256, _dt, False),    # tiled, ragged
         (1, 8, 2, 130, 400, 256, _dt, True),    # tiled, causal, Lq < Lkv
         (2, 8, 2, 7, 1000, 256, _dt, False),    # vector
         (1, 8, 1, 4, 2085, 256, _dt, True),     # vector, causal, 32 packed rows
         (2, 16, 4, 8, 4099, 256, _dt, False),   # vector, several splits
+        # head dim 256, forward and dQ keys split over 8 workgroups (16-row dQ waves)
+        (1, 2, 1, 128, 1024, 256, _dt, False),  # 8 splits
+        (1, 2, 2, 300, 1000, 256, _dt, True),   # 8 splits, causal with Lq < Lkv, last split empty
     ]
 
 
