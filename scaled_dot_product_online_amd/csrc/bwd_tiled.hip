@@ -907,10 +907,7 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q,
                      nsplit, dk_part, dv_part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  const int64_t kv_rows = s.B * s.Hkv * s.Lkv;
-  e = launch_split_reduce(s, out, nsplit, dk_part, dk, kv_rows, scale, st);
-  if (e != hipSuccess) return e;
-  return launch_split_reduce(s, out, nsplit, dv_part, dv, kv_rows, 1.f, st);
+  return launch_split_reduce_pair(s, out, nsplit, dk_part, dk, scale, dv_part, dv, 1.f, s.B * s.Hkv * s.Lkv, st);
 }
 
 template <typename T, int D, typename OutT>

@@ -88,6 +88,12 @@ hipError_t launch_split_combine(const Shape& s, Dt out, int nsplit, const float*
 hipError_t launch_split_reduce(const Shape& s, Dt out, int nsplit, const float* part, void* out_ptr, int64_t rows,
                                float scale, hipStream_t st);
 
+// Both reductions of a split dK/dV kernel in one launch: out_a from part_a with scale_a and
+// out_b from part_b with scale_b, each as launch_split_reduce (vector_path.hip).
+hipError_t launch_split_reduce_pair(const Shape& s, Dt out, int nsplit, const float* part_a, void* out_a,
+                                    float scale_a, const float* part_b, void* out_b, float scale_b, int64_t rows,
+                                    hipStream_t st);
+
 // Short-query path (vector_path.hip).
 int vector_num_splits(const Shape& s);
 size_t vector_fwd_workspace(const Shape& s);

@@ -716,6 +716,32 @@ __global__ __launch_bounds__(kThreads) void vec_dq_reduce_kernel(const float* __
   Store4<OutT>::run(dq + e4 * 4, x0 * scale, x1 * scale, x2 * scale, x3 * scale);
 }
 
+// Two such reductions in one launch (the dK and dV partials of a split dK/dV kernel):
+// workgroups [0, nb) take (part_a, out_a, scale_a), the rest (part_b, out_b, scale_b), each
+// over n4 groups of 4 columns, summed in split order as above.
+template <typename OutT>
+__global__ __launch_bounds__(kThreads) void vec_pair_reduce_kernel(const float* __restrict__ part_a,
+                                                                   OutT* __restrict__ out_a, float scale_a,
+                                                                   const float* __restrict__ part_b,
+                                                                   OutT* __restrict__ out_b, float scale_b,
+                                                                   int64_t n4, int nb, int nsplit) {
+  const bool second = (int)blockIdx.x >= nb;
+  const float* part = second ? part_b : part_a;
+  OutT* out = second ? out_b : out_a;
+  const float scale = second ? scale_b : scale_a;
+  const int64_t e4 = (int64_t)(blockIdx.x - (second ? nb : 0)) * kThreads + threadIdx.x;
+  if (e4 >= n4) return;
+  float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const f32x4_t a = *(const f32x4_t*)(part + (int64_t)sp * n4 * 4 + e4 * 4);
+    x0 += a[0];
+    x1 += a[1];
+    x2 += a[2];
+    x3 += a[3];
+  }
+  Store4<OutT>::run(out + e4 * 4, x0 * scale, x1 * scale, x2 * scale, x3 * scale);
+}
+
 // The combine kernel over `nsplit` partials [nsplit][B*Hq*Lq][D] and (m, l) pairs.
 template <int D, typename OutT>
 hipError_t combine_typed(const Shape& s, int nsplit, const float* part_o, const float* part_ml, const float* sinks,
@@ -827,6 +853,24 @@ hipError_t launch_split_combine(const Shape& s, Dt out, int nsplit, const float*
     default: return hipErrorInvalidValue;
   }
 #undef SDPA_COMBINE
+}
+
+hipError_t launch_split_reduce_pair(const Shape& s, Dt out, int nsplit, const float* part_a, void* out_a,
+                                    float scale_a, const float* part_b, void* out_b, float scale_b, int64_t rows,
+                                    hipStream_t st) {
+  const int64_t n4 = rows * (s.D / 4);
+  const int nb = (int)((n4 + kThreads - 1) / kThreads);
+  const dim3 grid((unsigned)(2 * nb));
+  if (out == kF32)
+    hipLaunchKernelGGL((vec_pair_reduce_kernel<float>), grid, dim3(kThreads), 0, st, part_a, (float*)out_a, scale_a,
+                       part_b, (float*)out_b, scale_b, n4, nb, nsplit);
+  else if (out == kBF16)
+    hipLaunchKernelGGL((vec_pair_reduce_kernel<bf16_t>), grid, dim3(kThreads), 0, st, part_a, (bf16_t*)out_a,
+                       scale_a, part_b, (bf16_t*)out_b, scale_b, n4, nb, nsplit);
+  else
+    hipLaunchKernelGGL((vec_pair_reduce_kernel<f16_t>), grid, dim3(kThreads), 0, st, part_a, (f16_t*)out_a,
+                       scale_a, part_b, (f16_t*)out_b, scale_b, n4, nb, nsplit);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_reduce(const Shape& s, Dt out, int nsplit, const float* part, void* out_ptr, int64_t rows,
