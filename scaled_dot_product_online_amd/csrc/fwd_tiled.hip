@@ -44,8 +44,8 @@ constexpr int kFwdThreads = 256;
 // Keys per tile: 64, or 32 at D = 256, where the O accumulators alone take 128 registers
 // per lane and a 64-key score block would not fit beside them. Every head dim runs two
 // waves per SIMD (two workgroups per CU): at D = 256 that leaves 256 registers per lane
-// for 128 of accumulators and 64 of Q operands, and a few values kept for the epilogue
-// spill outside the key loop (measured 16-29% faster than one wave per SIMD).
+// for 128 of accumulators and 64 of Q operands (the masked instantiation spills a few
+// registers; measured 16-29% faster than one wave per SIMD).
 template <int D>
 constexpr int fwd_bn() {
   return D == 256 ? 32 : 64;
