@@ -6,7 +6,7 @@ masked entry points) in a graph and replay it. Each case captures one forward +
 backward with static buffers, replays the graph several times with unrelated eager
 work and a synchronisation between the replays, and checks every replay bit for bit
 against the eager call on the same inputs. Covers the tiled, short-query and float32
-paths, causal and masked with sinks.
+paths, causal and masked with sinks, and head dim 256.
 """
 
 import pytest
@@ -22,6 +22,8 @@ CASES = [
     (1, 4, 2, 70, 130, 64, "f16", False, True),       # tiled with a mask
     (1, 4, 1, 256, 1024, 64, "f16", False, True),     # tiled, small grid: every kernel split 4 ways
     (1, 2, 2, 40, 60, 32, "f32", True, False),        # float32 path
+    (1, 4, 2, 130, 260, 256, "f16", True, False),     # head dim 256: two-wave forward, 16-row dQ
+    (1, 4, 2, 150, 300, 256, "bf16", False, True),    # head dim 256 with a mask (the forward spills registers)
 ]
 
 
