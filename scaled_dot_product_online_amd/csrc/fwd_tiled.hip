@@ -46,9 +46,12 @@ constexpr int kFwdThreads = 256;
 // waves per SIMD (two workgroups per CU): at D = 256 that leaves 256 registers per lane
 // for 128 of accumulators and 64 of Q operands (the masked instantiation spills a few
 // registers; measured 16-29% faster than one wave per SIMD).
-template <int D>
+// Without a mask, D <= 64 takes 128-key tiles: the per-tile costs (barrier, row maximum,
+// rescale test, copy issue) over twice the products (2-8% faster measured; with a mask the
+// larger tile ran slower).
+template <int D, bool MASKED>
 constexpr int fwd_bn() {
-  return D == 256 ? 32 : 64;
+  return D == 256 ? 32 : (D <= 64 && !MASKED) ? 128 : 64;
 }
 
 template <typename T, int D, bool CAUSAL, bool MASKED, typename OutT>
@@ -58,7 +61,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
     float scale_log2, Mask mask, const float* __restrict__ sinks, int nsplit, int split_tiles,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   using TL = SwzTile<D>;
-  constexpr int kFwdBN = fwd_bn<D>();
+  constexpr int kFwdBN = fwd_bn<D, MASKED>();
   constexpr int TILE = kFwdBN * TL::RB;  // bytes of one K or V tile
   // [buffer][K, V] tiles; buffer t & 1 holds key tile t while tile t + 1 streams into the other.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
@@ -313,7 +316,7 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const float* s
   const int n_qblk = (int)((s.Lq + kFwdBM - 1) / kFwdBM);
   const int n_bh = (int)(s.B * s.Hq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
-  constexpr int BN = fwd_bn<D>();
+  constexpr int BN = fwd_bn<D, M>();
   const int nt = (int)((s.Lkv + BN - 1) / BN);
   const int nsplit = tiled_fwd_splits(s);
   const int split_tiles = (nt + nsplit - 1) / nsplit;
@@ -354,7 +357,8 @@ hipError_t launch_d(const Shape& s, Dt out, bool causal, const Mask& mask, const
 }  // namespace
 
 // Key splits: enough workgroups for two per CU (256 CUs), each split keeping at least 4 key
-// tiles on average, at most 16 splits. (Doubling the target under a causal mask, where about
+// tiles of 64 keys on average (counted in 64-key tiles whatever the instantiation's tile, so
+// that the count, and the workspace, do not depend on the mask), at most 16 splits. (Doubling the target under a causal mask, where about
 // half of the split workgroups have little work, measured slower at one batch of 8 heads,
 // L = 2048: the partials cost more than the shorter critical path saves.)
 int tiled_fwd_splits(const Shape& s) {
