@@ -12,8 +12,9 @@
 // (batch, query head); each wave owns 32 rows. Key/value tiles of 64 rows (32 at D = 256,
 // 128 at D <= 64 without a mask) are copied into LDS by direct buffer-to-LDS loads
 // (range-checked, so rows past the end arrive as zeros), double-buffered so that tile
-// t+1 streams in while tile t is consumed, and shared by the 4 waves. Tiles are stored unpadded with an XOR
-// swizzle of 16-byte chunks (SwzTile) that keeps both read patterns conflict-free.
+// t+1 streams in while tile t is consumed, and shared by the 4 waves. Tiles are stored
+// unpadded with an XOR swizzle of 16-byte chunks (SwzTile) that keeps both read patterns
+// conflict-free.
 //
 // Orientation: the scores are computed transposed, S^T = K Q^T, so that in the
 // 32x32 accumulator each lane holds 16 scores of ONE query row (lanes l and
