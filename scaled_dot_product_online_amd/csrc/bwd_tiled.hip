@@ -560,7 +560,13 @@ template <int D>
 constexpr int kv_waves() {
   return D == 256 ? 4 : 8;
 }
-constexpr int kKvBM = 64;  // queries per tile
+constexpr int kKvBM = 64;  // queries per tile (the split count's unit)
+// Queries per tile of an instantiation: 128 at D <= 64 without a mask (the per-tile costs
+// over twice the products), else kKvBM.
+template <int D, bool HAS_MASK>
+constexpr int kv_bm() {
+  return (D <= 64 && !HAS_MASK) ? 128 : kKvBM;
+}
 
 // SPLIT: one of several workgroups that share a key block's (head, query tile) sequence
 // and write fp32 partials (a separate instantiation, so that the unsplit kernel is unchanged).
@@ -578,8 +584,10 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   using TL = SwzTile<D, 16>;
   constexpr int kKvWaves = kv_waves<D>();
   constexpr int kKvBN = 16 * kKvWaves;  // key rows per workgroup
-  constexpr int TILE = kKvBM * TL::RB;
-  constexpr int STAT = kKvBM * 8;       // {LSE*log2e, -Delta} of the tile's queries
+  constexpr int BM = kv_bm<D, HAS_MASK>();
+  constexpr int QB = BM / 16, NCC = BM / 32, PPC = QB / 2;  // 16-query blocks, 32-query chunks, pairs
+  constexpr int TILE = BM * TL::RB;
+  constexpr int STAT = BM * 8;       // {LSE*log2e, -Delta} of the tile's queries
   constexpr int BUF = 2 * TILE + STAT;  // one buffer: Q tile, dO tile, stats
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
 
@@ -624,13 +632,13 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     }
 
   const int co = Lkv - Lq;  // causal offset: key j visible to query i iff j <= i + co
-  const int q_begin = CAUSAL ? (max(0, kblk * kKvBN - co) / kKvBM) * kKvBM : 0;
-  const int ntiles = (Lq - q_begin + kKvBM - 1) / kKvBM;
+  const int q_begin = CAUSAL ? (max(0, kblk * kKvBN - co) / BM) * BM : 0;
+  const int ntiles = (Lq - q_begin + BM - 1) / BM;
   // (head, query tile) pairs, query tiles from the last one backward and the G heads of
   // each tile together: every workgroup of a KV group starts at the same (last) tile, so
   // the workgroups that run at once stream the same Q / dO tiles and share them in L2.
   const int total = G * ntiles;
-  auto tile_of = [&](int it) { return q_begin + (ntiles - 1 - it / G) * kKvBM; };
+  auto tile_of = [&](int it) { return q_begin + (ntiles - 1 - it / G) * BM; };
   // This split's part of the sequence (all of it without splits).
   const int per = SPLIT ? (total + nsplit - 1) / nsplit : total;
   const int it_lo = SPLIT ? min(total, split * per) : 0, it_hi = SPLIT ? min(total, it_lo + per) : total;
@@ -640,7 +648,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   const int ft0 = TL::f(trow);
   const int tcol = 8 * (L16 & 1);  // byte within the 16-byte chunk
   const int tch = (L16 & 3) >> 1;  // chunk 2*db + tch
-  const typename TL::template DmaPlan<kKvBM, kKvWaves> dma(wave, lane);
+  const typename TL::template DmaPlan<BM, kKvWaves> dma(wave, lane);
   auto issue = [&](int it, uint8_t* buf) {
     const int gi = it % G, t0 = tile_of(it);
     const int64_t head = (int64_t)(b * Hq + hk * G + gi);
@@ -652,7 +660,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     }
   };
   constexpr int NC = D / 32;       // 32-wide steps of the S / dP contraction over d
-  constexpr int NCS = 2 * (D / 32);  // stages of the dV / dK products: (c', pair of 16-wide d blocks)
+  constexpr int NCS = NCC * (D / 32);  // stages of the dV / dK products: (c', pair of 16-wide d blocks)
 
   // One query tile. The LDS operand reads of each stage are issued one stage ahead of the
   // matrix-core instructions that use them; sched_fence() keeps the compiler from sinking
@@ -667,12 +675,12 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     // addresses derived from them inside the loop instead of keeping each one live.
     int fa = fa0, ft = ft0, q4x4 = 4 * q4;
     asm volatile("" : "+v"(fa), "+v"(ft), "+v"(q4x4));
-    // Stage a of the S / dP products: d step c = a / 2, query blocks 2*(a % 2) + 0, 1.
+    // Stage a of the S / dP products: d step c = a / PPC, query blocks 2*(a % PPC) + 0, 1.
     auto load_a = [&](int a, u32x4_t* qa, u32x4_t* da) {
-      const int c = a / 2;
+      const int c = a / PPC;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int off = ((2 * (a % 2) + h) * 16 + n16) * TL::RB + ((4 * c + q4) ^ fa) * 16;
+        const int off = ((2 * (a % PPC) + h) * 16 + n16) * TL::RB + ((4 * c + q4) ^ fa) * 16;
         qa[h] = *(const u32x4_t*)(qt + off);
         da[h] = *(const u32x4_t*)(dt + off);
       }
@@ -695,35 +703,42 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     float kbias = 0.f;
     if constexpr (HAS_MASK)
       if (mask.sq == 0) kbias = mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh);
-    // Row statistics of this lane's queries qm*16 + 4*q4 + j.
-    f32x4_t sa[4], sb[4];
+    // Row statistics of this lane's queries qm*16 + 4*q4 + j: {LSE*log2e, -Delta} pairs, held
+    // in registers over the tile at 64 queries, read from LDS where they are used at 128.
+    constexpr bool kStatRegs = QB <= 4;
+    f32x4_t sreg[kStatRegs ? 2 * QB : 1];
+    if constexpr (kStatRegs) {
 #pragma unroll
-    for (int qm = 0; qm < 4; ++qm) {
-      const int qi0 = qm * 16 + 4 * q4;
-      sa[qm] = st[qi0 / 2];
-      sb[qm] = st[qi0 / 2 + 1];
+      for (int i = 0; i < 2 * QB; ++i) sreg[i] = st[((i >> 1) * 16 + 4 * q4) / 2 + (i & 1)];
     }
+    auto stat = [&](int qm, int half) {
+      if constexpr (kStatRegs)
+        return sreg[2 * qm + half];
+      else
+        return st[(qm * 16 + 4 * q4) / 2 + half];
+    };
     u32x4_t qa[2][2], da[2][2];
     load_a(0, qa[0], da[0]);
     sched_fence();
 
     // S = Q K^T and dP - Delta = dO V^T - Delta (Delta enters as the accumulator's start)
     // in 16-query blocks qm: lane (n16, q4) holds queries qm*16 + 4*q4 + j of key krow.
-    f32x4_t s[4], dp[4];
+    f32x4_t s[QB], dp[QB];
 #pragma unroll
-    for (int qm = 0; qm < 4; ++qm) {
+    for (int qm = 0; qm < QB; ++qm) {
+      const f32x4_t sa = stat(qm, 0), sb = stat(qm, 1);
       s[qm] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-      dp[qm] = (f32x4_t){sa[qm][1], sa[qm][3], sb[qm][1], sb[qm][3]};
+      dp[qm] = (f32x4_t){sa[1], sa[3], sb[1], sb[3]};
     }
     u32x2_t tb[2][8];
 #pragma unroll
-    for (int a = 0; a < 2 * NC; ++a) {
-      if (a + 1 < 2 * NC) load_a(a + 1, qa[(a + 1) & 1], da[(a + 1) & 1]);
+    for (int a = 0; a < PPC * NC; ++a) {
+      if (a + 1 < PPC * NC) load_a(a + 1, qa[(a + 1) & 1], da[(a + 1) & 1]);
       else load_c(0, tb[0]);
-      const int c = a / 2;
+      const int c = a / PPC;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int qm = 2 * (a % 2) + h;
+        const int qm = 2 * (a % PPC) + h;
         s[qm] = mfma16<T>(qa[a & 1][h], kop[c], s[qm]);
         dp[qm] = mfma16<T>(da[a & 1][h], vop[c], dp[qm]);
       }
@@ -733,16 +748,17 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     // P and dS as B operands; chunk c' (32 queries): e = 0..3 -> block 2c', e = 4..7 -> block 2c'+1.
     // Only the softmax is duplicated for the masked case (a wave-uniform branch), so
     // both paths share the same registers.
-    u32x4_t pop[2], dsop[2];
+    u32x4_t pop[NCC], dsop[NCC];
     auto softmax = [&](auto edge_tag) {
       constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
+      for (int cc = 0; cc < NCC; ++cc) {
         float pv[8], dsv[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int qm = 2 * cc + h;
-          const float l2[4] = {sa[qm][0], sa[qm][2], sb[qm][0], sb[qm][2]};
+          const f32x4_t sa = stat(qm, 0), sb = stat(qm, 1);
+          const float l2[4] = {sa[0], sa[2], sb[0], sb[2]};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float nb = -l2[j];
@@ -801,9 +817,9 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     const uint8_t* dt = qt + TILE;
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = tile_of(it);
-    if (CAUSAL && t0 + kKvBM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
+    if (CAUSAL && t0 + BM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
     if (!wave_keys) continue;
-    tile((t0 + kKvBM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G);  // wave-uniform flag
+    tile((t0 + BM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G);  // wave-uniform flag
   }
   if constexpr (SPLIT) {  // one split: fp32 partials of dK / scale and dV, [split][b*Hkv*Lkv + hk*Lkv + key]
     if (krow < Lkv) {
