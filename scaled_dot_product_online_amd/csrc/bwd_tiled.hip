@@ -20,7 +20,8 @@
 //   tiles and 32-key tiles, which fits two waves per SIMD.
 // Kernel 2 (dkv_kernel): one workgroup = 8 waves x 16 key rows of one (b, hk);
 //   the waves keep K and V of their rows in registers and accumulate dK and dV
-//   while streaming Q/dO tiles of 64 queries of every query head of the group.
+//   while streaming Q/dO tiles of 64 queries (128 at D <= 64 without a mask) of every
+//   query head of the group.
 //   Scores are computed as S = Q K^T on 16x16x32 tiles (lane owns one key
 //   column), which puts P and dS directly in the B-operand layout of
 //   dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are read with the LDS
@@ -553,7 +554,8 @@ __global__ __launch_bounds__(64 * kDq16Waves, 1) void dq16_kernel(
 // One workgroup = 8 waves x 16 key rows = 128 keys of one (b, hk). Each wave keeps K and
 // V of its 16 keys as B operands and the dK^T, dV^T accumulators in registers (16x16x32
 // matrix-core tiles keep that state at 96 registers per lane for D = 128, so two waves
-// share a SIMD), and streams Q/dO tiles of 64 queries of every query head of the group.
+// share a SIMD), and streams Q/dO tiles of 64 queries (128 at D <= 64 without a mask, see
+// kv_bm) of every query head of the group.
 // At D = 256 that state is 192 registers, so the workgroup has 4 waves (64 keys), one
 // per SIMD, each with the whole register file.
 template <int D>
