@@ -16,7 +16,10 @@ Prints ONE JSON line (rank 0, N=1). Besides the contract fields it carries:
   vector_path   the short-query path (Lq = 8, D = 128, Lkv = 8192) in HBM GB/s: forward,
                 backward end to end (both stages), and the backward's streaming kernel
                 (stage 0) alone
-Options: --sweep prints one line per workload instead (no CPU baseline).
+  graph         device times from HIP graph replays (no host launch gaps): a whole step
+                from a graph of R steps, and each stage from a graph of R launches of it
+                (--graph-reps R, 0 turns it off)
+Options: --sweep prints one line per workload instead.
 """
 
 from __future__ import annotations
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-vector", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--graph-reps", type=int, default=10, metavar="R",
+                    help="also time each stage as R launches replayed from a HIP graph (0: off)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run 3 plain device copies of MIB MiB (reference for HBM traffic counters)")
     return ap.parse_args()
@@ -92,7 +97,9 @@ class Runner:
         wb = sd.workspace_bytes(1, B, Hq, Hkv, Lq, Lkv, D, causal, code)
         self.ws_f = torch.empty(max(wf, 256), dtype=torch.uint8, device=device)
         self.ws_b = torch.empty(max(wb, 256), dtype=torch.uint8, device=device)
-        self.stream = torch.cuda.current_stream(device)
+        # A stream of its own (default priority), so that the stages can also be captured
+        # in HIP graphs (capture needs a stream other than the null stream).
+        self.stream = torch.cuda.Stream(device)
         self.tdt = tdt
         self.fwd_flops = flops(B, Hq, Lq, Lkv, D, causal)
         self.bwd_flops = flops(B, Hq, Lq, Lkv, D, causal, backward=True)
@@ -142,6 +149,41 @@ class Runner:
             ms["bwd_stage0"] += e[1].elapsed_time(e[2]) / steps
             ms["bwd_stage1"] += e[2].elapsed_time(e[3]) / steps
         return wall, ms
+
+    def graph_times(self, reps, rounds):
+        """Device times without host launch gaps, from HIP graphs replayed between two events on
+        the launch stream (median over `rounds` replays): `step` is one whole step (forward,
+        dQ stage, dK/dV stage) from a graph of `reps` steps; each stage's entry is one launch
+        from a graph of `reps` launches of that stage alone (so it runs after itself, with
+        its own operands still in the caches). Where a stage's device time is shorter than a
+        host call through the binding, the eager times above include the host's gaps."""
+        torch = self.torch
+        stages = (("fwd", self.fwd), ("bwd_stage0", lambda: self.bwd(0)), ("bwd_stage1", lambda: self.bwd(1)))
+
+        def whole_step():
+            for _, fn in stages:
+                fn()
+
+        graphs = {}
+        for key, fn in stages + (("step", whole_step),):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                for _ in range(reps):
+                    fn()
+            graphs[key] = g
+        torch.cuda.synchronize()
+        times = {key: [] for key in graphs}
+        with torch.cuda.stream(self.stream):
+            for _ in range(rounds):
+                for key, g in graphs.items():
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(self.stream)
+                    g.replay()
+                    e1.record(self.stream)
+                    torch.cuda.synchronize()
+                    times[key].append(e0.elapsed_time(e1) / reps)
+        del graphs
+        return {key: float(np.median(v)) for key, v in times.items()}
 
 
 def blas_info():
@@ -206,7 +248,7 @@ def cpu_baseline(case, budget_s=10.0, mask=None, sinks=None):
                       f"forward+backward ({t_all:.1f} s); value = fwd+bwd FLOPs counted as for the GPU / fwd+bwd time"}
 
 
-def measure(runner, steps, warmup):
+def measure(runner, steps, warmup, graph_reps=0):
     wall, ms = runner.timed(steps, warmup)
     total = runner.fwd_flops + runner.bwd_flops
     value = total * steps / wall / 1e12
@@ -216,6 +258,11 @@ def measure(runner, steps, warmup):
            "bwd_tflops": runner.bwd_flops / ((ms["bwd_stage0"] + ms["bwd_stage1"]) * 1e-3) / 1e12}
     out["fwd_frac_of_peak"] = out["fwd_tflops"] / PEAK_TFLOPS[dt]
     out["fwdbwd_frac_of_peak"] = value / PEAK_TFLOPS[dt]
+    if graph_reps > 0:
+        g = runner.graph_times(graph_reps, max(3, min(steps, 10)))
+        step = g.pop("step")
+        out["graph"] = {"reps": graph_reps, "step_ms": step, "fwdbwd_tflops": total / (step * 1e-3) / 1e12,
+                        "kernel_ms": g, "fwd_tflops": runner.fwd_flops / (g["fwd"] * 1e-3) / 1e12}
     dom = max(ms, key=ms.get)
     if runner.path == "vector":
         algo = {"fwd": runner.fwd_bytes, "bwd_stage0": runner.bwd_bytes, "bwd_stage1": 0}[dom]
@@ -275,15 +322,23 @@ def measured_traffic(runner, label):
     return None
 
 
-def vector_line(device, steps, warmup):
+def vector_line(device, steps, warmup, graph_reps=0):
     r = Runner(VECTOR_WORKLOAD, device)
     _, ms = r.timed(steps, warmup)
     fwd_gbs = r.fwd_bytes / (ms["fwd"] * 1e-3) / 1e9
     bwd_gbs = r.bwd_bytes / ((ms["bwd_stage0"] + ms["bwd_stage1"]) * 1e-3) / 1e9
     main_gbs = r.bwd_bytes / (ms["bwd_stage0"] * 1e-3) / 1e9  # the streaming kernel alone (stage 0)
-    return {"workload": VECTOR_WORKLOAD, "kernel_ms": ms, "fwd_GBps": fwd_gbs, "bwd_GBps": bwd_gbs,
-            "fwd_frac_of_hbm_peak": fwd_gbs / PEAK_HBM_GBS, "bwd_frac_of_hbm_peak": bwd_gbs / PEAK_HBM_GBS,
-            "bwd_stage0_frac_of_hbm_peak": main_gbs / PEAK_HBM_GBS}
+    out = {"workload": VECTOR_WORKLOAD, "kernel_ms": ms, "fwd_GBps": fwd_gbs, "bwd_GBps": bwd_gbs,
+           "fwd_frac_of_hbm_peak": fwd_gbs / PEAK_HBM_GBS, "bwd_frac_of_hbm_peak": bwd_gbs / PEAK_HBM_GBS,
+           "bwd_stage0_frac_of_hbm_peak": main_gbs / PEAK_HBM_GBS}
+    if graph_reps > 0:
+        g = r.graph_times(graph_reps, max(3, min(steps, 10)))
+        step = g.pop("step")
+        out["graph"] = {"reps": graph_reps, "step_ms": step, "kernel_ms": g,
+                        "fwd_frac_of_hbm_peak": r.fwd_bytes / (g["fwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                        "bwd_frac_of_hbm_peak": r.bwd_bytes / ((g["bwd_stage0"] + g["bwd_stage1"]) * 1e-3) / 1e9
+                        / PEAK_HBM_GBS}
+    return out
 
 
 def config_of(name):
@@ -319,7 +374,7 @@ def main():
     names = [w[0] for w in WORKLOADS] if args.sweep else [args.workload]
     for name in names:
         r = Runner(name, device, rotate=args.sweep and BY_NAME[name][4] <= 8)
-        m = measure(r, args.steps, args.warmup)
+        m = measure(r, args.steps, args.warmup, args.graph_reps)
         line = {"metric": METRIC, "value": m["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True,
                 "scaling": "weak", "vs_baseline": None, "dtype": r.case.dtype, "data": "synthetic",
@@ -327,8 +382,10 @@ def main():
                 "bwd_tflops": m["bwd_tflops"], "fwd_frac_of_peak": m["fwd_frac_of_peak"],
                 "fwdbwd_frac_of_peak": m["fwdbwd_frac_of_peak"], "kernel_ms": m["kernel_ms"],
                 "roofline": m["roofline"]}
+        if "graph" in m:
+            line["graph"] = m["graph"]
         if not args.sweep and not args.no_vector:
-            line["vector_path"] = vector_line(device, args.steps, args.warmup)
+            line["vector_path"] = vector_line(device, args.steps, args.warmup, args.graph_reps)
         if args.sweep:
             line["kv_copies"] = len(r.kv)
         mask, sinks = mask_and_sinks(name)
