@@ -163,7 +163,11 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
 
   // One key tile. As in the dK/dV kernel, each stage's LDS reads are issued one stage
   // ahead of the matrix-core instructions that use them, behind scheduling fences.
-  auto tile = [&](bool masked, const uint8_t* kt, const uint8_t* vt, int kt0) {
+  // Key padding (a boolean mask that varies only along keys): tiles whose keys are all
+  // padding are skipped, and the others take each key's keep flag from a ballot of the
+  // mask bytes, which are read a tile ahead (no per-score mask loads).
+  const bool pad = HAS_MASK && is_key_padding(mask);
+  auto tile = [&](bool masked, const uint8_t* kt, const uint8_t* vt, int kt0, uint64_t keep) {
     // Lane constants made opaque per tile, so that the compiler rebuilds the LDS addresses
     // derived from them inside the loop instead of keeping each one live across it.
     // Chunk 2c + g of row n sits at (2c ^ (g ^ f(n))); chunk 4db + tx of row r at (4db ^ (tx ^ f(r))).
@@ -215,14 +219,17 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
       // dS^T as B operands, one per 16-key half c2. Only the softmax is duplicated for
       // the masked case (a wave-uniform branch), so both paths share the same registers.
       u32x4_t dsop[2];
-      auto softmax = [&](auto edge_tag) {
+      // PAD: bits 8r + j of lm keep key kt0 + kb*32 + 8r + 4g + j (the lane's element 4r + j).
+      const uint32_t lm = (uint32_t)(keep >> (32 * kb)) >> (4 * g);
+      auto softmax = [&](auto edge_tag, auto pad_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
+        constexpr bool PAD = decltype(pad_tag)::value;
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           float ds[8];
           // The mask's bias of keys kt0 + kb*32 + 8*(2*c2 + h) + 4g + 0..3 (element e = 4h + j).
           float bias[8];
-          if constexpr (HAS_MASK) {
+          if constexpr (HAS_MASK && !PAD) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int key0 = kt0 + kb * 32 + 8 * (2 * c2 + h) + 4 * g;
@@ -240,20 +247,23 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
           for (int e = 0; e < 8; ++e) {
             const int i = 8 * c2 + e;
             float nb = -lse2;
-            if constexpr (HAS_MASK) nb = bias[e] - lse2;
+            if constexpr (HAS_MASK && !PAD) nb = bias[e] - lse2;
             float p = exp2_le1(fmaf(s[i], scale_log2, nb));
             if constexpr (EDGE)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
               p = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) < klim ? p : 0.f;
+            if constexpr (PAD) p = ((lm >> (8 * (i >> 2) + (i & 3))) & 1u) ? p : 0.f;
             ds[e] = p * (dp[i] - dlt);
           }
           dsop[c2] = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]),
                                pack2<T>(ds[6], ds[7])};
         }
       };
-      if (masked)
-        softmax(std::true_type{});
+      if (HAS_MASK && pad)  // no causal mask with a mask; keys past the end have no bit
+        softmax(std::false_type{}, std::true_type{});
+      else if (masked)
+        softmax(std::true_type{}, std::false_type{});
       else
-        softmax(std::false_type{});
+        softmax(std::false_type{}, std::false_type{});
       sched_fence();
       // dQ^T += K^T dS^T.
 #pragma unroll
@@ -277,8 +287,6 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
     dma.fill(srd_rows<D>(kbase, Lkv, t_lo * kDqBN), b0, wave);
     dma.fill(srd_rows<D>(vbase, Lkv, t_lo * kDqBN), b0 + TILE, wave);
   }
-  // Key padding: tiles whose keys are all padding are skipped (mask bytes read a tile ahead).
-  const bool pad = HAS_MASK && is_key_padding(mask);
   uint32_t kept_next = pad && t_lo < t_hi ? key_kept(mask, b, t_lo * kDqBN, kDqBN, Lkv, lane) : 1u;
   for (int t = t_lo; t < t_hi; ++t) {
     wait_vmem();
@@ -294,8 +302,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
     const uint8_t* vt = kt + TILE;
     const int kt0 = t * kDqBN;
     if (CAUSAL && kt0 > q0 + 31 + co) continue;
-    if (pad && !__any(kept != 0u)) continue;  // every key of the tile is padding
-    tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0 + co), kt, vt, kt0);  // wave-uniform flag
+    const uint64_t keep = pad ? __ballot(kept != 0u) : 0;  // bit j: key kt0 + j kept
+    if (pad && keep == 0) continue;                           // every key of the tile is padding
+    tile((kt0 + kDqBN > Lkv) || (CAUSAL && kt0 + kDqBN - 1 > q0 + co), kt, vt, kt0, keep);  // wave-uniform flag
   }
   if (dq_part != nullptr) {  // one key split: fp32 partial of dQ / scale, [split][b*Hq*Lq + hq*Lq + q]
     if (row_ok) {
@@ -673,7 +682,19 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   const int64_t mkey = HAS_MASK ? (int64_t)b * mask.sb + (int64_t)min(krow, Lkv - 1) : 0;
   // A key-padding mask that removes all 16 keys of this wave leaves dK = dV = 0: no tile work.
   const bool wave_keys = !(HAS_MASK && is_key_padding(mask)) || __any(key_kept(mask, b, kw0, 16, Lkv, lane) != 0u);
-  auto tile = [&](bool masked, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0, int hq) {
+  // One that removes every key of the workgroup: no tile is streamed at all (every wave
+  // takes the same decision, so no barrier is left unmatched); dK = dV = 0 is written below.
+  bool wg_keys = true;
+  if constexpr (HAS_MASK) {
+    if (is_key_padding(mask)) {
+      uint32_t kk = 0u;
+#pragma unroll
+      for (int r = 0; r < kKvBN / 64; ++r) kk |= key_kept(mask, b, kblk * kKvBN + 64 * r, 64, Lkv, lane);
+      wg_keys = __any(kk != 0u);
+    }
+  }
+  const int it_end = wg_keys ? it_hi : it_lo;
+  auto tile = [&](bool masked, const uint8_t* qt, const uint8_t* dt, const f32x4_t* st, int t0, int hq, float kbias) {
     // Lane constants made opaque per tile, so that the compiler recomputes the LDS
     // addresses derived from them inside the loop instead of keeping each one live.
     int fa = fa0, ft = ft0, q4x4 = 4 * q4;
@@ -701,11 +722,6 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
       }
     };
 
-    // A mask that does not vary along queries (stride 0: key padding) has one bias per
-    // lane and tile.
-    float kbias = 0.f;
-    if constexpr (HAS_MASK)
-      if (mask.sq == 0) kbias = mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)hq * mask.sh);
     // Row statistics of this lane's queries qm*16 + 4*q4 + j: {LSE*log2e, -Delta} pairs, held
     // in registers over the tile at 64 queries, read from LDS where they are used at 128.
     constexpr bool kStatRegs = QB <= 4;
@@ -811,18 +827,35 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     }
   };
 
-  if (it_lo < it_hi) issue(it_lo, lds + (it_lo & 1) * BUF);
-  for (int it = it_lo; it < it_hi; ++it) {
+  // A mask that does not vary along queries (key padding, or a per-head key bias) has one
+  // bias per lane (its key) and query head. It is read one step ahead, before that step's
+  // tile copies are issued, and taken into a register right after the step's copy wait:
+  // read inside the step, its wait would also cover the next tile's copies, which the
+  // wait counter orders before it.
+  const bool kbias_step = HAS_MASK && mask.sq == 0;
+  auto kbias_of = [&](int it) {
+    return mask_bias_log2<T>(mask.p, mask.kind, mkey + (int64_t)(hk * G + it % G) * mask.sh);
+  };
+  float kbias_next = 0.f;
+  if (kbias_step && it_lo < it_end) kbias_next = kbias_of(it_lo);
+  if (it_lo < it_end) issue(it_lo, lds + (it_lo & 1) * BUF);
+  for (int it = it_lo; it < it_end; ++it) {
     wait_vmem();
     __syncthreads();
-    if (it + 1 < it_hi) issue(it + 1, lds + ((it + 1) & 1) * BUF);
+    float kbias = 0.f;
+    if constexpr (HAS_MASK) {
+      kbias = kbias_next;
+      asm volatile("" : "+v"(kbias));  // the load's wait here, with nothing else in flight
+      if (kbias_step && it + 1 < it_end) kbias_next = kbias_of(it + 1);
+    }
+    if (it + 1 < it_end) issue(it + 1, lds + ((it + 1) & 1) * BUF);
     const uint8_t* qt = lds + (it & 1) * BUF;
     const uint8_t* dt = qt + TILE;
     const f32x4_t* st = (const f32x4_t*)(qt + 2 * TILE);
     const int t0 = tile_of(it);
     if (CAUSAL && t0 + BM - 1 + co < kw0) continue;  // no query of the tile sees this wave's keys
     if (!wave_keys) continue;
-    tile((t0 + BM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G);  // wave-uniform flag
+    tile((t0 + BM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G, kbias);  // wave-uniform flag
   }
   if constexpr (SPLIT) {  // one split: fp32 partials of dK / scale and dV, [split][b*Hkv*Lkv + hk*Lkv + key]
     if (krow < Lkv) {

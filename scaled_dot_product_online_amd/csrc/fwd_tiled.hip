@@ -198,7 +198,21 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
       sched_fence();
     }
 
-    if constexpr (MASKED) {  // every tile: s <- s*scale*log2e + bias, keys past the end -inf
+    if (MASKED && D <= 128 && pad) {
+      // Key padding: the keep flags of the tile's keys are already in registers (one byte per
+      // lane, read a tile ahead); a ballot gathers them, bit j for key kt0 + j (keys past
+      // the end read as dropped), and each score takes its key's bit. (At D = 256 the
+      // general path below, which spills fewer registers there.)
+      const uint64_t keep = __ballot(kept != 0u);
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+        // Bits 8r + j of lm: key kt0 + kb*32 + 8r + 4g + j, the lane's element 4r + j.
+        const uint32_t lm = (uint32_t)(keep >> (32 * kb)) >> (4 * g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[kb][i] = ((lm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[kb][i] * scale_log2 : -INFINITY;
+      }
+    } else if constexpr (MASKED) {  // every tile: s <- s*scale*log2e + bias, keys past the end -inf
 #pragma unroll
       for (int kb = 0; kb < kFwdBN / 32; ++kb)
 #pragma unroll
