@@ -21,7 +21,8 @@
 // Kernel 2 (dkv_kernel): one workgroup = 8 waves x 16 key rows of one (b, hk);
 //   the waves keep K and V of their rows in registers and accumulate dK and dV
 //   while streaming Q/dO tiles of 64 queries (128 at D <= 64 without a mask) of every
-//   query head of the group.
+//   query head of the group. At D = 256 the workgroup's K rows sit in LDS instead and
+//   the query tiles are 32 rows, which fits two waves per SIMD.
 //   Scores are computed as S = Q K^T on 16x16x32 tiles (lane owns one key
 //   column), which puts P and dS directly in the B-operand layout of
 //   dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are read with the LDS
@@ -561,29 +562,37 @@ __global__ __launch_bounds__(64 * kDq16Waves, 1) void dq16_kernel(
 // ---------------------------------------------------------------------------------
 // Stage 1: dK, dV
 // ---------------------------------------------------------------------------------
-// One workgroup = 8 waves x 16 key rows = 128 keys of one (b, hk). Each wave keeps K and
-// V of its 16 keys as B operands and the dK^T, dV^T accumulators in registers (16x16x32
-// matrix-core tiles keep that state at 96 registers per lane for D = 128, so two waves
-// share a SIMD), and streams Q/dO tiles of 64 queries (128 at D <= 64 without a mask, see
+// One workgroup = 8 waves x 16 key rows = 128 keys of one (b, hk), two waves per SIMD.
+// Each wave keeps K and V of its 16 keys as B operands and the dK^T, dV^T accumulators in
+// registers (16x16x32 matrix-core tiles keep that state at 96 registers per lane for
+// D = 128), and streams Q/dO tiles of 64 queries (128 at D <= 64 without a mask, see
 // kv_bm) of every query head of the group.
-// At D = 256 that state is 192 registers, so the workgroup has 4 waves (64 keys), one
-// per SIMD, each with the whole register file.
+// At D = 256 that state would be 192 registers, too many for two waves per SIMD beside the
+// scores and operand staging: there the workgroup's 128 K rows are copied into LDS once
+// (64 KiB) and each wave reads its K^T operands from there per contraction step, the query
+// tiles are 32 rows, and the wave keeps V and the accumulators (160 registers). Against 4
+// waves of 16 keys at one wave per SIMD with K in registers: 28-38% faster, one more LDS
+// read per step.
 template <int D>
 constexpr int kv_waves() {
-  return D == 256 ? 4 : 8;
+  return 8;
+}
+template <int D>
+constexpr bool kv_k_lds() {
+  return D == 256;
 }
 constexpr int kKvBM = 64;  // queries per tile (the split count's unit)
 // Queries per tile of an instantiation: 128 at D <= 64 without a mask (the per-tile costs
-// over twice the products), else kKvBM.
+// over twice the products), 32 at D = 256, else kKvBM.
 template <int D, bool HAS_MASK>
 constexpr int kv_bm() {
-  return (D <= 64 && !HAS_MASK) ? 128 : kKvBM;
+  return D == 256 ? 32 : (D <= 64 && !HAS_MASK) ? 128 : kKvBM;
 }
 
 // SPLIT: one of several workgroups that share a key block's (head, query tile) sequence
 // and write fp32 partials (a separate instantiation, so that the unsplit kernel is unchanged).
 template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT, bool SPLIT>
-__global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_per_eu(kv_waves<D>() / 4, kv_waves<D>() / 4))) void dkv_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkv_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const uint16_t* __restrict__ dO,
@@ -601,7 +610,10 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   constexpr int TILE = BM * TL::RB;
   constexpr int STAT = BM * 8;       // {LSE*log2e, -Delta} of the tile's queries
   constexpr int BUF = 2 * TILE + STAT;  // one buffer: Q tile, dO tile, stats
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
+  constexpr bool KLDS = kv_k_lds<D>();
+  constexpr int KT = KLDS ? kKvBN * TL::RB : 0;  // the workgroup's K rows (KLDS)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KT + 2 * BUF];
+  uint8_t* const lds = lds_all + KT;
 
   // Low block ids carry the key blocks that see the most causal queries (dispatched
   // first), then the split, then the KV group. With n_bhk a multiple of 8, dispatch
@@ -621,17 +633,21 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   const int64_t kvoff = (int64_t)bhk * Lkv * D;
   const rsrc_t rk = make_rsrc(k + kvoff, (uint32_t)Lkv * D * 2);
   const rsrc_t rv = make_rsrc(v + kvoff, (uint32_t)Lkv * D * 2);
-  u32x4_t kop[D / 32], vop[D / 32];
+  u32x4_t kop[KLDS ? 1 : D / 32], vop[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     const uint32_t e = (uint32_t)(krow * D + 32 * c + 8 * q4) * 2;
-    kop[c] = buf_load16(rk, e);
+    if constexpr (!KLDS) kop[c] = buf_load16(rk, e);
     vop[c] = buf_load16(rv, e);
   }
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    settle(kop[c]);
+    if constexpr (!KLDS) settle(kop[c]);
     settle(vop[c]);
+  }
+  if constexpr (KLDS) {  // the K rows of the workgroup, copied once (waited with the first tile)
+    const typename TL::template DmaPlan<kKvBN, kKvWaves> kdma(wave, lane);
+    kdma.fill(srd_rows<D>(k + kvoff, Lkv, kblk * kKvBN), lds_all, wave);
   }
   // dK^T, dV^T: block db holds d = 16*db + 4*q4 + i of key krow.
   f32x4_t dka[D / 16], dva[D / 16];
@@ -700,7 +716,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     int fa = fa0, ft = ft0, q4x4 = 4 * q4;
     asm volatile("" : "+v"(fa), "+v"(ft), "+v"(q4x4));
     // Stage a of the S / dP products: d step c = a / PPC, query blocks 2*(a % PPC) + 0, 1.
-    auto load_a = [&](int a, u32x4_t* qa, u32x4_t* da) {
+    auto load_a = [&](int a, u32x4_t* qa, u32x4_t* da, u32x4_t& ka) {
       const int c = a / PPC;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -708,6 +724,10 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
         qa[h] = *(const u32x4_t*)(qt + off);
         da[h] = *(const u32x4_t*)(dt + off);
       }
+      // K^T operand of step c: row wave*16 + n16 of the K rows, whose swizzle equals that
+      // of row n16 (it depends on the row's low 3 bits).
+      if constexpr (KLDS)
+        if (a % PPC == 0) ka = *(const u32x4_t*)(lds_all + (wave * 16 + n16) * TL::RB + ((4 * c + q4) ^ fa) * 16);
     };
     auto load_c = [&](int si, u32x2_t* tb) {
       const int cc = si / (D / 32), dbp = si % (D / 32);
@@ -724,7 +744,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
 
     // Row statistics of this lane's queries qm*16 + 4*q4 + j: {LSE*log2e, -Delta} pairs, held
     // in registers over the tile at 64 queries, read from LDS where they are used at 128.
-    constexpr bool kStatRegs = QB <= 4;
+    constexpr bool kStatRegs = QB <= 4 && !KLDS;
     f32x4_t sreg[kStatRegs ? 2 * QB : 1];
     if constexpr (kStatRegs) {
 #pragma unroll
@@ -736,8 +756,8 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
       else
         return st[(qm * 16 + 4 * q4) / 2 + half];
     };
-    u32x4_t qa[2][2], da[2][2];
-    load_a(0, qa[0], da[0]);
+    u32x4_t qa[2][2], da[2][2], ka[2];
+    load_a(0, qa[0], da[0], ka[0]);
     sched_fence();
 
     // S = Q K^T and dP - Delta = dO V^T - Delta (Delta enters as the accumulator's start)
@@ -752,13 +772,13 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     u32x2_t tb[2][8];
 #pragma unroll
     for (int a = 0; a < PPC * NC; ++a) {
-      if (a + 1 < PPC * NC) load_a(a + 1, qa[(a + 1) & 1], da[(a + 1) & 1]);
+      if (a + 1 < PPC * NC) load_a(a + 1, qa[(a + 1) & 1], da[(a + 1) & 1], ka[((a + 1) / PPC) & 1]);
       else load_c(0, tb[0]);
       const int c = a / PPC;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int qm = 2 * (a % PPC) + h;
-        s[qm] = mfma16<T>(qa[a & 1][h], kop[c], s[qm]);
+        s[qm] = mfma16<T>(qa[a & 1][h], KLDS ? ka[c & 1] : kop[KLDS ? 0 : c], s[qm]);
         dp[qm] = mfma16<T>(da[a & 1][h], vop[c], dp[qm]);
       }
       sched_fence();
@@ -857,6 +877,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     if (!wave_keys) continue;
     tile((t0 + BM > Lq) || (CAUSAL && t0 + co < kw0 + 15), qt, dt, st, t0, hk * G + it % G, kbias);  // wave-uniform flag
   }
+  if constexpr (KLDS) wait_vmem();  // the K copy, when no tile waited for it
   if constexpr (SPLIT) {  // one split: fp32 partials of dK / scale and dV, [split][b*Hkv*Lkv + hk*Lkv + key]
     if (krow < Lkv) {
       const int64_t po = ((int64_t)split * n_bhk + bhk) * Lkv * D + (int64_t)krow * D;
@@ -898,7 +919,7 @@ int dq_splits(const Shape& s) {
   return split_count((s.Lq + kDqBM - 1) / kDqBM * s.B * s.Hq, 2 * 256, (s.Lkv + bn - 1) / bn);
 }
 int dkv_splits(const Shape& s, bool causal) {
-  const int64_t bn = s.D == 256 ? 64 : 128;  // 16 keys per wave
+  const int64_t bn = 128;  // 8 waves x 16 keys
   return split_count((s.Lkv + bn - 1) / bn * s.B * s.Hkv, (causal ? 2 : 1) * 256,
                      (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM));
 }
