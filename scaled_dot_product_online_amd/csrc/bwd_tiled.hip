@@ -609,7 +609,12 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   constexpr int QB = BM / 16, NCC = BM / 32, PPC = QB / 2;  // 16-query blocks, 32-query chunks, pairs
   constexpr int TILE = BM * TL::RB;
   constexpr int STAT = BM * 8;       // {LSE*log2e, -Delta} of the tile's queries
-  constexpr int BUF = 2 * TILE + STAT;  // one buffer: Q tile, dO tile, stats
+  // A mask that varies along queries, with aligned rows (vec4), is copied tile by tile into
+  // LDS with Q and dO: the tile's BM query rows of the workgroup's keys, row-major, 16-bit
+  // elements at most. Read from global memory per score instead, a lane (one key) walks
+  // down a column of the mask.
+  constexpr int MT = HAS_MASK ? BM * kKvBN * 2 : 0;
+  constexpr int BUF = 2 * TILE + STAT + MT;  // one buffer: Q tile, dO tile, stats, mask block
   constexpr bool KLDS = kv_k_lds<D>();
   constexpr int KT = KLDS ? kKvBN * TL::RB : 0;  // the workgroup's K rows (KLDS)
   __shared__ __attribute__((aligned(1024))) uint8_t lds_all[KT + 2 * BUF];
@@ -677,6 +682,7 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   const int tcol = 8 * (L16 & 1);  // byte within the 16-byte chunk
   const int tch = (L16 & 3) >> 1;  // chunk 2*db + tch
   const typename TL::template DmaPlan<BM, kKvWaves> dma(wave, lane);
+  const bool mtile = HAS_MASK && mask.sq != 0 && mask.vec4;
   auto issue = [&](int it, uint8_t* buf) {
     const int gi = it % G, t0 = tile_of(it);
     const int64_t head = (int64_t)(b * Hq + hk * G + gi);
@@ -685,6 +691,23 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     if (wave == kKvWaves - 1 && lane < STAT / 16) {
       const srd_t rs = make_srd(rowstat + head * lq_pad + t0, (uint32_t)(Lq - t0) * 8);
       dma16(rs, buf + 2 * TILE, (uint32_t)(16 * lane));
+    }
+    if constexpr (HAS_MASK) {
+      if (mtile) {
+        const int es = mask.kind == kMaskBool ? 1 : 2;
+        const int lpr = kKvBN * es / 16, rpi = 64 / lpr;  // lanes per row, rows per 1 KiB copy
+        const int64_t e0 = (int64_t)b * mask.sb + (int64_t)(hk * G + gi) * mask.sh + (int64_t)t0 * mask.sq +
+                           (int64_t)kblk * kKvBN;
+        // Elements from e0 through key Lkv - 1 of query row Lq - 1: rows past the end (and
+        // keys past the end in the last row) arrive as zeros.
+        const int64_t nel = (int64_t)(Lq - 1 - t0) * mask.sq + (Lkv - kblk * kKvBN);
+        const srd_t rm =
+            make_srd((const uint8_t*)mask.p + e0 * es, (uint32_t)min(nel * es, (int64_t)0xffffffffll));
+        for (int i = wave; i < BM / rpi; i += kKvWaves) {
+          const int r = i * rpi + lane / lpr;
+          dma16(rm, buf + 2 * TILE + STAT + 1024 * i, (uint32_t)(r * mask.sq * es + (lane % lpr) * 16));
+        }
+      }
     }
   };
   constexpr int NC = D / 32;       // 32-wide steps of the S / dP contraction over d
@@ -788,8 +811,13 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
     // Only the softmax is duplicated for the masked case (a wave-uniform branch), so
     // both paths share the same registers.
     u32x4_t pop[NCC], dsop[NCC];
-    auto softmax = [&](auto edge_tag) {
+    // MK: 0 = no mask, a mask constant along queries (kbias) or one read per score; 1 / 2 = a
+    // boolean / additive mask block in LDS (this lane's column: key wave*16 + n16).
+    const uint8_t* mb = qt + 2 * TILE + STAT;
+    const int mcol = wave * 16 + n16;
+    auto softmax = [&](auto edge_tag, auto mk_tag) {
       constexpr bool EDGE = decltype(edge_tag)::value;
+      constexpr int MK = decltype(mk_tag)::value;
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) {
         float pv[8], dsv[8];
@@ -801,7 +829,11 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             float nb = -l2[j];
-            if constexpr (HAS_MASK) {  // bias of (query t0 + qm*16 + 4*q4 + j, key krow)
+            if constexpr (HAS_MASK && MK == 1) {  // bias of (query t0 + qm*16 + 4*q4 + j, key krow)
+              nb += mb[(qm * 16 + 4 * q4 + j) * kKvBN + mcol] ? 0.f : -INFINITY;
+            } else if constexpr (HAS_MASK && MK == 2) {
+              nb += to_f32<T>(((const uint16_t*)mb)[(qm * 16 + 4 * q4 + j) * kKvBN + mcol]) * kLog2e;
+            } else if constexpr (HAS_MASK) {
               if (mask.sq == 0) {
                 nb += kbias;
               } else {
@@ -824,10 +856,23 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
                              pack2<T>(dsv[6], dsv[7])};
       }
     };
+    auto run_softmax = [&](auto edge_tag) {
+      if constexpr (HAS_MASK) {
+        if (mtile && mask.kind == kMaskBool) {
+          softmax(edge_tag, std::integral_constant<int, 1>{});
+          return;
+        }
+        if (mtile) {
+          softmax(edge_tag, std::integral_constant<int, 2>{});
+          return;
+        }
+      }
+      softmax(edge_tag, std::integral_constant<int, 0>{});
+    };
     if (masked)
-      softmax(std::true_type{});
+      run_softmax(std::true_type{});
     else
-      softmax(std::false_type{});
+      run_softmax(std::false_type{});
     sched_fence();
 
     // dV^T += dO^T P and dK^T += Q^T dS: A operands transposed out of LDS, rows

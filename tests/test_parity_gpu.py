@@ -66,11 +66,14 @@ for _dt in ("f16", "bf16"):
         (1, 2, 1, 96, 700, 96, _dt, False),     # 2 splits, head dim 96
         # backward splits on small grids: dK/dV over its (query head, query tile) sequence
         (1, 8, 1, 512, 256, 64, _dt, False),    # 16 splits, GQA 8:1
-        (1, 4, 1, 256, 200, 256, _dt, False),   # 4 splits, head dim 256 (4-wave workgroups)
-        # head dim 256 (32-key forward / dQ tiles, 16-row dQ waves, 4-wave dK/dV, 2-wave short-query kernels)
+        (1, 4, 1, 256, 200, 256, _dt, False),   # 4 splits, head dim 256
+        # head dim 256 (32-key forward / dQ tiles, 16-row dQ waves, dK/dV with K rows in LDS and
+        # 32-query tiles, 2-wave short-query kernels)
         (1, 4, 2, 200, 200, 256, _dt, True),    # tiled, causal
         (1, 4, 1, 70, 300, 256, _dt, False),    # tiled, ragged
         (1, 8, 2, 130, 400, 256, _dt, True),    # tiled, causal, Lq < Lkv
+        (2, 8, 1, 33, 129, 256, _dt, False),    # tiled: one key past a 128-key block, one query past a 32-query tile
+        (1, 4, 4, 96, 96, 256, _dt, True),      # tiled, MHA, causal: three 32-query tiles
         (2, 8, 2, 7, 1000, 256, _dt, False),    # vector
         (1, 8, 1, 4, 2085, 256, _dt, True),     # vector, causal, 32 packed rows
         (2, 16, 4, 8, 4099, 256, _dt, False),   # vector, several splits
