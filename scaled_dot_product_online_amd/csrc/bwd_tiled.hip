@@ -78,6 +78,12 @@ constexpr int dq_bn() {
   return D == 256 ? 32 : (D <= 64 && !HAS_MASK) ? 128 : 64;
 }
 
+// The dQ kernel stages a mask through LDS (mask_staged) at D <= 96.
+template <int D>
+__host__ __device__ inline bool dq_mask_staged(const Mask& m) {
+  return D <= 96 && mask_staged(m);
+}
+
 // D <= 128 (D = 256 runs dq16_kernel).
 template <typename T, int D, bool CAUSAL, bool HAS_MASK, typename OutT>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restrict__ q,
@@ -168,6 +174,13 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
   // padding are skipped, and the others take each key's keep flag from a ballot of the
   // mask bytes, which are read a tile ahead (no per-score mask loads).
   const bool pad = HAS_MASK && is_key_padding(mask);
+  // A boolean mask that varies along queries (mask_staged), at D <= 96: its block for each
+  // key tile (the workgroup's 128 query rows, the tile's keys, one byte each) is copied into
+  // dynamic LDS with K and V, double-buffered, and read from there. (At D = 128 the masked
+  // kernel already holds 256 registers and the staged path would spill.)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_mask[];
+  constexpr int MBLK = kDqBM * kDqBN;
+  const bool mstage = HAS_MASK && dq_mask_staged<D>(mask);
   auto tile = [&](bool masked, const uint8_t* kt, const uint8_t* vt, int kt0, uint64_t keep) {
     // Lane constants made opaque per tile, so that the compiler rebuilds the LDS addresses
     // derived from them inside the loop instead of keeping each one live across it.
@@ -234,7 +247,15 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const int key0 = kt0 + kb * 32 + 8 * (2 * c2 + h) + 4 * g;
-              if (mask.vec4 && key0 < Lkv) {
+              if (D <= 96 && mstage) {  // this lane's row of the tile's staged block
+                const uint8_t* mblk = lds_mask + ((kt0 / kDqBN) & 1) * MBLK + (wave * 32 + n) * kDqBN + 4 * g;
+                mask_bias4_bool_word(*(const uint32_t*)(mblk + kb * 32 + 8 * (2 * c2 + h)), bias + 4 * h);
+                if constexpr (EDGE) {  // keys past the end (the last tile only)
+#pragma unroll
+                  for (int j = 0; j < 4; ++j)
+                    if (key0 + j >= Lkv) bias[4 * h + j] = -INFINITY;
+                }
+              } else if (mask.vec4 && key0 < Lkv) {
                 mask_bias4_log2<T>(mask.p, mask.kind, mrow + key0, bias + 4 * h);
               } else {
 #pragma unroll
@@ -283,10 +304,23 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
   const uint16_t* kbase = k + kvoff;
   const uint16_t* vbase = v + kvoff;
   const typename TL::template DmaPlan<kDqBN, 4> dma(wave, lane);
+  auto stage_mask = [&](int t) {  // 16 bytes per lane, kDqBN / 16 lanes per row
+    constexpr int LPR = kDqBN / 16, RPI = 64 / LPR;
+    const int kt0 = t * kDqBN, r0 = qblk * kDqBM;
+    const int64_t e0 = (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)r0 * mask.sq + kt0;
+    const int64_t nel = (int64_t)(Lq - 1 - r0) * mask.sq + (Lkv - kt0);  // through row Lq - 1, key Lkv - 1
+    const srd_t rm = make_srd((const uint8_t*)mask.p + e0, (uint32_t)min(nel, (int64_t)0xffffffffll));
+    uint8_t* mb = lds_mask + (t & 1) * MBLK;
+    for (int i = wave; i < kDqBM / RPI; i += 4) {
+      const int r = i * RPI + lane / LPR;
+      dma16(rm, mb + 1024 * i, (uint32_t)(r * mask.sq + (lane % LPR) * 16));
+    }
+  };
   if (t_lo < t_hi) {
     uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
     dma.fill(srd_rows<D>(kbase, Lkv, t_lo * kDqBN), b0, wave);
     dma.fill(srd_rows<D>(vbase, Lkv, t_lo * kDqBN), b0 + TILE, wave);
+    if (mstage) stage_mask(t_lo);
   }
   uint32_t kept_next = pad && t_lo < t_hi ? key_kept(mask, b, t_lo * kDqBN, kDqBN, Lkv, lane) : 1u;
   for (int t = t_lo; t < t_hi; ++t) {
@@ -296,6 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
       uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
       dma.fill(srd_rows<D>(kbase, Lkv, (t + 1) * kDqBN), nb, wave);
       dma.fill(srd_rows<D>(vbase, Lkv, (t + 1) * kDqBN), nb + TILE, wave);
+      if (mstage) stage_mask(t + 1);
     }
     const uint32_t kept = kept_next;
     if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * kDqBN, kDqBN, Lkv, lane);
@@ -1003,7 +1038,8 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q,
                          (const uint16_t*)dO, (OutT*)dq, rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh,
                          lq_pad, scale_log2, scale, mask, nsplit, (nt + nsplit - 1) / nsplit, dq_part);
     else
-      hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kThreads), 0, st,
+      hipLaunchKernelGGL((dq_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kThreads),
+                         (M && dq_mask_staged<D>(mask)) ? 2 * (size_t)kDqBM * BN : 0, st,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const OutT*)o, lse,
                          (const uint16_t*)dO, (OutT*)dq, rowstat, (int)s.Hq, G, (int)s.Lq, (int)s.Lkv, n_qblk, n_bh,
                          lq_pad, scale_log2, scale, mask, nsplit, (nt + nsplit - 1) / nsplit, dq_part);

@@ -374,6 +374,11 @@ __device__ __forceinline__ void mask_bias4_log2(const void* p, int kind, int64_t
     b[3] = hi_f32<T>(w[1]) * kLog2e;
   }
 }
+// The biases of 4 boolean mask bytes held in one word (byte j: key j), in log2 units.
+__device__ __forceinline__ void mask_bias4_bool_word(uint32_t w, float* b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = ((w >> (8 * j)) & 0xffu) ? 0.f : -INFINITY;
+}
 __device__ __forceinline__ float load_f32(const bf16_t* p) { return to_f32<bf16_t>(p->bits); }
 
 __device__ __forceinline__ float load_f32(const f16_t* p) { return to_f32<f16_t>(p->bits); }

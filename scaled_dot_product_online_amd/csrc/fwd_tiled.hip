@@ -138,10 +138,29 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
   const uint16_t* kbase = k + kvoff;
   const uint16_t* vbase = v + kvoff;
   const typename TL::template DmaPlan<kFwdBN, 4> dma(wave, lane);
+  // A boolean mask that varies along queries (mask_staged): the block of the workgroup's
+  // 128 query rows and the tile's keys is copied into dynamic LDS ([buffer][row][key], one
+  // byte each) with K and V, 8 lanes of 16 bytes per row; rows past Lq arrive as zeros.
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_mask[];
+  constexpr int MBLK = kFwdBM * kFwdBN;  // bytes of one buffer's mask block
+  const bool mstage = MASKED && mask_staged(mask);
+  auto stage_mask = [&](int t) {
+    constexpr int LPR = kFwdBN / 16, RPI = 64 / LPR;  // lanes per row, rows per 1 KiB copy
+    const int kt0 = t * kFwdBN, r0 = qblk * kFwdBM;
+    const int64_t e0 = (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)r0 * mask.sq + kt0;
+    const int64_t nel = (int64_t)(Lq - 1 - r0) * mask.sq + (Lkv - kt0);  // through row Lq - 1, key Lkv - 1
+    const srd_t rm = make_srd((const uint8_t*)mask.p + e0, (uint32_t)min(nel, (int64_t)0xffffffffll));
+    uint8_t* mb = lds_mask + (t & 1) * MBLK;
+    for (int i = wave; i < kFwdBM / RPI; i += 4) {
+      const int r = i * RPI + lane / LPR;
+      dma16(rm, mb + 1024 * i, (uint32_t)(r * mask.sq + (lane % LPR) * 16));
+    }
+  };
   if (t_lo < t_hi) {
     uint8_t* b0 = lds + (t_lo & 1) * 2 * TILE;
     dma.fill(srd_rows<D>(kbase, Lkv, t_lo * kFwdBN), b0, wave);
     dma.fill(srd_rows<D>(vbase, Lkv, t_lo * kFwdBN), b0 + TILE, wave);
+    if (mstage) stage_mask(t_lo);
   }
   // Key padding: a tile whose keys are all padding adds nothing and is skipped; its mask
   // bytes are read one tile ahead.
@@ -154,6 +173,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
       uint8_t* nb = lds + ((t + 1) & 1) * 2 * TILE;
       dma.fill(srd_rows<D>(kbase, Lkv, (t + 1) * kFwdBN), nb, wave);
       dma.fill(srd_rows<D>(vbase, Lkv, (t + 1) * kFwdBN), nb + TILE, wave);
+      if (mstage) stage_mask(t + 1);
     }
     const uint32_t kept = kept_next;
     if (pad && t + 1 < t_hi) kept_next = key_kept(mask, b, (t + 1) * kFwdBN, kFwdBN, Lkv, lane);
@@ -212,6 +232,19 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
         for (int i = 0; i < 16; ++i)
           s[kb][i] = ((lm >> (8 * (i >> 2) + (i & 3))) & 1u) ? s[kb][i] * scale_log2 : -INFINITY;
       }
+    } else if (MASKED && D <= 128 && mstage) {  // a staged boolean mask: as below, the flags from LDS
+      const uint8_t* mrow_l = lds_mask + (t & 1) * MBLK + (wave * 32 + n) * kFwdBN + 4 * g;  // this lane's row
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {  // keys key0 .. key0 + 3
+          const int key0 = kt0 + kb * 32 + 8 * i4 + 4 * g;
+          float bias[4];
+          mask_bias4_bool_word(*(const uint32_t*)(mrow_l + kb * 32 + 8 * i4), bias);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            s[kb][4 * i4 + j] = key0 + j < Lkv ? fmaf(s[kb][4 * i4 + j], scale_log2, bias[j]) : -INFINITY;
+        }
     } else if constexpr (MASKED) {  // every tile: s <- s*scale*log2e + bias, keys past the end -inf
 #pragma unroll
       for (int kb = 0; kb < kFwdBN / 32; ++kb)
@@ -219,7 +252,11 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
         for (int i4 = 0; i4 < 4; ++i4) {  // keys key0 .. key0 + 3
           const int key0 = kt0 + kb * 32 + 8 * i4 + 4 * g;
           float bias[4];
-          if (mask.vec4 && key0 < Lkv) {
+          if (D == 256 && mstage) {  // (at D = 256 the branch inside the loop spills fewer registers)
+            mask_bias4_bool_word(
+                *(const uint32_t*)(lds_mask + (t & 1) * MBLK + (wave * 32 + n) * kFwdBN + kb * 32 + 8 * i4 + 4 * g),
+                bias);
+          } else if (mask.vec4 && key0 < Lkv) {
             mask_bias4_log2<T>(mask.p, mask.kind, mrow + key0, bias);
           } else {
 #pragma unroll
@@ -338,7 +375,8 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const float* s
   float* part_o = nsplit > 1 ? (float*)ws : nullptr;
   float* part_ml = nsplit > 1 ? part_o + (int64_t)nsplit * s.B * s.Hq * s.Lq * s.D : nullptr;
   // With key splits the sink joins in the combine kernel, once per row.
-  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kFwdThreads), 0, st,
+  const size_t mshm = (M && mask_staged(mask)) ? 2 * (size_t)kFwdBM * BN : 0;  // staged mask blocks
+  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kFwdThreads), mshm, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, (int)s.Hq,
                      (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, mask,
                      nsplit > 1 ? nullptr : sinks, nsplit, split_tiles, part_o, part_ml);

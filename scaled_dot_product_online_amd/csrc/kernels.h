@@ -36,6 +36,11 @@ constexpr Mask kNoMask = {nullptr, kMaskNone, 0, 0, 0, 0};
 __device__ __forceinline__ bool is_key_padding(const Mask& mask) {
   return mask.kind == kMaskBool && mask.sq == 0 && mask.sh == 0;
 }
+// A boolean mask that varies along queries, with aligned rows (vec4): the tiled forward and
+// dQ kernels copy its block for each key tile into LDS with K and V (dynamic LDS, one byte
+// per query row and key of a tile, two buffers) instead of reading it per score from global
+// memory. Launchers and kernels decide it with this same test.
+__host__ __device__ inline bool mask_staged(const Mask& m) { return m.kind == kMaskBool && m.sq != 0 && m.vec4; }
 // For such a mask: this lane's key key0 + lane of batch b, nonzero when kept (lanes >= n
 // and keys past the end read 0). A kernel loads the bytes of its next key tile one step
 // ahead and tests them with __any() when it gets there.
