@@ -37,6 +37,9 @@ for _dt in ("f16", "bf16"):
         (1, 4, 2, 200, 200, 64, _dt, False, None, None, 0, True),            # sinks only
         (1, 4, 2, 150, 170, 128, _dt, True, None, None, 0, True),            # causal + sinks
         (1, 4, 2, 130, 900, 128, _dt, False, "bool", "full", 2, True),       # tiled, 3 key splits
+        # a boolean mask staged through LDS by the forward and (D <= 96) dQ kernels: ragged
+        # query rows and keys (Lkv not a whole number of key tiles)
+        (2, 4, 2, 150, 260, 96, _dt, False, "bool", "shared", 1, False),
         (1, 2, 1, 100, 800, 64, _dt, True, None, None, 0, True),             # causal + sinks, 3 key splits
         (1, 8, 2, 256, 300, 128, _dt, False, "bool", "keypad", 0, True),     # dK/dV in 4 splits
         # contiguous key padding (batch b keeps its first keys, one batch none): whole key
