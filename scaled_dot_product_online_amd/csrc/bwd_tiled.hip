@@ -148,6 +148,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
       HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
   // -Delta: the dK/dV kernel starts its dP accumulators from it.
   if (row_ok && g == 0 && split == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, -dlt};
+  f32x16_t ndlt;  // -Delta of this lane's query in every element (the dP chains' start)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndlt[i] = -dlt;
 
   f32x16_t acc[D / 32];
 #pragma unroll
@@ -227,7 +230,9 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
         if (c + SD - 1 < NC) load_s(kb, c + SD - 1, kv[(c + SD - 1) % SD]);
         else if (c + SD - 1 == NC) load_q(kb, 0, tb[0]);
         s = mfma32<T>(kv[c % SD][0], qop[c], s);
-        dp = mfma32<T>(kv[c % SD][1], doop[c], dp);
+        // Without a mask the dP chain starts from -Delta (a block kept across the loop), so
+        // that dS = P * dP needs no subtraction per score.
+        dp = mfma32<T>(kv[c % SD][1], doop[c], (!HAS_MASK && c == 0) ? ndlt : dp);
         sched_fence();
       }
       // dS^T as B operands, one per 16-key half c2. Only the softmax is duplicated for
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(const uint16_t* __restr
             if constexpr (EDGE)  // key kt0 + kb*32 + 8*(i/4) + (i%4) + 4g below key_lim
               p = kt0 + kb * 32 + 8 * (i >> 2) + (i & 3) < klim ? p : 0.f;
             if constexpr (PAD) p = ((lm >> (8 * (i >> 2) + (i & 3))) & 1u) ? p : 0.f;
-            ds[e] = p * (dp[i] - dlt);
+            ds[e] = HAS_MASK ? p * (dp[i] - dlt) : p * dp[i];
           }
           dsop[c2] = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]),
                                pack2<T>(ds[6], ds[7])};
@@ -438,6 +443,7 @@ __global__ __launch_bounds__(64 * kDq16Waves, 1) void dq16_kernel(
       HAS_MASK ? (int64_t)b * mask.sb + (int64_t)hq * mask.sh + (int64_t)min(qrow, Lq - 1) * mask.sq : 0;
   // -Delta: the dK/dV kernel starts its dP accumulators from it.
   if (row_ok && q4 == 0 && split == 0) rowstat[(int64_t)bh * lq_pad + qrow] = (f32x2_t){lse2, -dlt};
+  const f32x4_t ndlt = {-dlt, -dlt, -dlt, -dlt};  // the dP chains' start without a mask (as in dq_kernel)
 
   // dQ^T block db: lane (n16, q4) holds d = 16*db + 4*q4 + i of query qrow.
   f32x4_t acc[D / 16];
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(64 * kDq16Waves, 1) void dq16_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = mfma16<T>(kv[c & 1][2 * kb], qop[c], s[kb]);
-        dp[kb] = mfma16<T>(kv[c & 1][2 * kb + 1], doop[c], dp[kb]);
+        dp[kb] = mfma16<T>(kv[c & 1][2 * kb + 1], doop[c], (!HAS_MASK && c == 0) ? ndlt : dp[kb]);
       }
       sched_fence();
     }
@@ -529,7 +535,7 @@ __global__ __launch_bounds__(64 * kDq16Waves, 1) void dq16_kernel(
           float p = exp2_le1(fmaf(s[kb][j], scale_log2, nb));
           if constexpr (EDGE)  // key kt0 + kb*16 + 4*q4 + j below key_lim
             p = kt0 + kb * 16 + j < klim ? p : 0.f;
-          ds[4 * kb + j] = p * (dp[kb][j] - dlt);
+          ds[4 * kb + j] = HAS_MASK ? p * (dp[kb][j] - dlt) : p * dp[kb][j];
         }
       }
       dsop = (u32x4_t){pack2<T>(ds[0], ds[1]), pack2<T>(ds[2], ds[3]), pack2<T>(ds[4], ds[5]), pack2<T>(ds[6], ds[7])};
