@@ -40,6 +40,8 @@ for _dt in ("f16", "bf16"):
         # a boolean mask staged through LDS by the forward and (D <= 96) dQ kernels: ragged
         # query rows and keys (Lkv not a whole number of key tiles)
         (2, 4, 2, 150, 260, 96, _dt, False, "bool", "shared", 1, False),
+        (2, 4, 2, 100, 132, 64, _dt, False, "bool", "head", 0, True),        # per-head block, staged
+        (2, 4, 2, 90, 200, 128, _dt, False, "bool", "full", 0, False),       # per-(batch, head) block
         (1, 2, 1, 100, 800, 64, _dt, True, None, None, 0, True),             # causal + sinks, 3 key splits
         (1, 8, 2, 256, 300, 128, _dt, False, "bool", "keypad", 0, True),     # dK/dV in 4 splits
         # contiguous key padding (batch b keeps its first keys, one batch none): whole key
