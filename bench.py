@@ -259,10 +259,14 @@ def measure(runner, steps, warmup, graph_reps=0):
     out["fwd_frac_of_peak"] = out["fwd_tflops"] / PEAK_TFLOPS[dt]
     out["fwdbwd_frac_of_peak"] = value / PEAK_TFLOPS[dt]
     if graph_reps > 0:
-        g = runner.graph_times(graph_reps, max(3, min(steps, 10)))
-        step = g.pop("step")
-        out["graph"] = {"reps": graph_reps, "step_ms": step, "fwdbwd_tflops": total / (step * 1e-3) / 1e12,
-                        "kernel_ms": g, "fwd_tflops": runner.fwd_flops / (g["fwd"] * 1e-3) / 1e12}
+        try:
+            g = runner.graph_times(graph_reps, max(3, min(steps, 10)))
+        except Exception as e:  # the contract's fields above stand without it
+            out["graph"] = {"error": f"{type(e).__name__}: {e}"}
+        else:
+            step = g.pop("step")
+            out["graph"] = {"reps": graph_reps, "step_ms": step, "fwdbwd_tflops": total / (step * 1e-3) / 1e12,
+                            "kernel_ms": g, "fwd_tflops": runner.fwd_flops / (g["fwd"] * 1e-3) / 1e12}
     dom = max(ms, key=ms.get)
     if runner.path == "vector":
         algo = {"fwd": runner.fwd_bytes, "bwd_stage0": runner.bwd_bytes, "bwd_stage1": 0}[dom]
@@ -332,7 +336,11 @@ def vector_line(device, steps, warmup, graph_reps=0):
            "fwd_frac_of_hbm_peak": fwd_gbs / PEAK_HBM_GBS, "bwd_frac_of_hbm_peak": bwd_gbs / PEAK_HBM_GBS,
            "bwd_stage0_frac_of_hbm_peak": main_gbs / PEAK_HBM_GBS}
     if graph_reps > 0:
-        g = r.graph_times(graph_reps, max(3, min(steps, 10)))
+        try:
+            g = r.graph_times(graph_reps, max(3, min(steps, 10)))
+        except Exception as e:
+            out["graph"] = {"error": f"{type(e).__name__}: {e}"}
+            return out
         step = g.pop("step")
         out["graph"] = {"reps": graph_reps, "step_ms": step, "kernel_ms": g,
                         "fwd_frac_of_hbm_peak": r.fwd_bytes / (g["fwd"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
