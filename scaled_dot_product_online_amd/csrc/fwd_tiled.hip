@@ -8,11 +8,12 @@
 // evaluated online over key tiles in the exp2 domain with fp32 state (same pull
 // request, "Implementation Notes": log2 domain, fp32 accumulators).
 //
-// Work decomposition: one workgroup = 4 waves = 128 query rows of one
-// (batch, query head); each wave owns 32 rows. Key/value tiles of 64 rows (32 at D = 256,
-// 128 at D <= 64 without a mask) are copied into LDS by direct buffer-to-LDS loads
-// (range-checked, so rows past the end arrive as zeros), double-buffered so that tile
-// t+1 streams in while tile t is consumed, and shared by the 4 waves. Tiles are stored
+// Work decomposition: one workgroup = 4 waves = 128 query rows of one (batch, query head)
+// (8 waves = 256 rows at D = 128 without a mask); each wave owns 32 rows. Key/value tiles
+// of 64 rows (32 at D = 256, 128 at D <= 64 and D = 128 without a mask) are copied into LDS
+// by direct buffer-to-LDS loads (range-checked, so rows past the end arrive as zeros),
+// double-buffered so that tile t+1 streams in while tile t is consumed, and shared by the
+// workgroup's waves. Tiles are stored
 // unpadded with an XOR swizzle of 16-byte chunks (SwzTile) that keeps both read patterns
 // conflict-free.
 //
@@ -40,29 +41,39 @@
 namespace sdpa {
 namespace {
 
-constexpr int kFwdBM = 128;  // query rows per workgroup
-constexpr int kFwdThreads = 256;
+constexpr int kFwdBM = 128;  // query rows per 4-wave workgroup (the key-split count's unit)
 // Keys per tile: 64, or 32 at D = 256, where the O accumulators alone take 128 registers
 // per lane and a 64-key score block would not fit beside them. Every head dim runs two
-// waves per SIMD (two workgroups per CU): at D = 256 that leaves 256 registers per lane
-// for 128 of accumulators and 64 of Q operands (the masked instantiation spills a few
-// registers; measured 16-29% faster than one wave per SIMD).
-// Without a mask, D <= 64 takes 128-key tiles: the per-tile costs (barrier, row maximum,
-// rescale test, copy issue) over twice the products (2-8% faster measured; with a mask the
-// larger tile ran slower).
+// waves per SIMD: at D = 256 that leaves 256 registers per lane for 128 of accumulators
+// and 64 of Q operands (the masked instantiation spills a few registers; measured 16-29%
+// faster than one wave per SIMD).
+// Without a mask, D <= 64 and D = 128 take 128-key tiles: the per-tile costs (barrier, row
+// maximum, rescale test, copy issue) over twice the products (2-8% faster measured at
+// D <= 64; with a mask the larger tile ran slower). At D = 128 two 128-key K/V buffers take
+// 128 KiB of LDS, so the workgroup grows to 8 waves (256 rows) for two waves per SIMD, with
+// K operands one stage ahead and the LDS address lane constants rebuilt per tile (256
+// registers, no spills): 4-6% faster without the causal mask, level with it.
 template <int D, bool MASKED>
 constexpr int fwd_bn() {
-  return D == 256 ? 32 : (D <= 64 && !MASKED) ? 128 : 64;
+  return D == 256 ? 32 : ((D <= 64 || D == 128) && !MASKED) ? 128 : 64;
+}
+// Waves per workgroup: 8 (256 query rows, one workgroup per CU) for unmasked D = 128 with
+// its 128-key tiles (two 64 KiB K/V buffers), else 4 (two workgroups per CU).
+template <int D, bool MASKED>
+constexpr int fwd_waves() {
+  return (D == 128 && !MASKED) ? 8 : 4;
 }
 
 template <typename T, int D, bool CAUSAL, bool MASKED, typename OutT>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
+__global__ __launch_bounds__((64 * fwd_waves<D, MASKED>()), (8 / fwd_waves<D, MASKED>())) void fwd_tiled_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     OutT* __restrict__ o, float* __restrict__ lse, int Hq, int G, int Lq, int Lkv, int n_qblk, int n_bh,
     float scale_log2, Mask mask, const float* __restrict__ sinks, int nsplit, int split_tiles,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   using TL = SwzTile<D>;
   constexpr int kFwdBN = fwd_bn<D, MASKED>();
+  constexpr int W = fwd_waves<D, MASKED>();
+  constexpr int kFwdBM = 32 * W;  // query rows per workgroup
   constexpr int TILE = kFwdBN * TL::RB;  // bytes of one K or V tile
   // [buffer][K, V] tiles; buffer t & 1 holds key tile t while tile t + 1 streams into the other.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * 2 * TILE];
@@ -137,10 +148,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
 
   const uint16_t* kbase = k + kvoff;
   const uint16_t* vbase = v + kvoff;
-  const typename TL::template DmaPlan<kFwdBN, 4> dma(wave, lane);
+  const typename TL::template DmaPlan<kFwdBN, W> dma(wave, lane);
   // A boolean mask that varies along queries (mask_staged): the block of the workgroup's
-  // 128 query rows and the tile's keys is copied into dynamic LDS ([buffer][row][key], one
-  // byte each) with K and V, 8 lanes of 16 bytes per row; rows past Lq arrive as zeros.
+  // query rows and the tile's keys is copied into dynamic LDS ([buffer][row][key], one
+  // byte each) with K and V, 16 bytes per lane; rows past Lq arrive as zeros.
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_mask[];
   constexpr int MBLK = kFwdBM * kFwdBN;  // bytes of one buffer's mask block
   const bool mstage = MASKED && mask_staged(mask);
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
     const int64_t nel = (int64_t)(Lq - 1 - r0) * mask.sq + (Lkv - kt0);  // through row Lq - 1, key Lkv - 1
     const srd_t rm = make_srd((const uint8_t*)mask.p + e0, (uint32_t)min(nel, (int64_t)0xffffffffll));
     uint8_t* mb = lds_mask + (t & 1) * MBLK;
-    for (int i = wave; i < kFwdBM / RPI; i += 4) {
+    for (int i = wave; i < kFwdBM / RPI; i += W) {
       const int r = i * RPI + lane / LPR;
       dma16(rm, mb + 1024 * i, (uint32_t)(r * mask.sq + (lane % LPR) * 16));
     }
@@ -183,11 +194,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
     if (CAUSAL && kt0 > q0 + 31 + co) continue;  // tile entirely above this wave's diagonal
     if (pad && !__any(kept != 0u)) continue;  // every key of the tile is padding
 
-    // At D = 256 (two waves per SIMD, 128 registers of O accumulators) the lane constants
-    // of the LDS addresses are made opaque per tile, so that the compiler rebuilds each
-    // stage's address inside the loop instead of keeping all 16 live across it.
+    // At D = 256 (two waves per SIMD, 128 registers of O accumulators) and with 128-key tiles
+    // at D = 128 (128 registers of scores) the lane constants of the LDS addresses are made
+    // opaque per tile, so that the compiler rebuilds each stage's address inside the loop
+    // instead of keeping all of them live across it.
     int fkx = fk, fvx = fv, fv8x = fv8, nrow = n * TL::RB;
-    if constexpr (D == 256) asm volatile("" : "+v"(fkx), "+v"(fvx), "+v"(fv8x), "+v"(nrow));
+    if constexpr (D == 256 || (D == 128 && kFwdBN == 128)) asm volatile("" : "+v"(fkx), "+v"(fvx), "+v"(fv8x), "+v"(nrow));
     // S^T = K Q^T: 32 keys x 32 queries per accumulator block.
     f32x16_t s[kFwdBN / 32];
 #pragma unroll
@@ -195,9 +207,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
     // K operands are read KD - 1 stages of the contraction ahead of the matrix-core
-    // instructions that use them (two, or one at D = 256 for registers), behind
-    // scheduling fences.
-    constexpr int KD = D == 256 ? 2 : 3;
+    // instructions that use them (two, or one at D = 256 and with 128-key tiles at D = 128,
+    // for registers), behind scheduling fences.
+    constexpr int KD = (D == 256 || (D == 128 && kFwdBN == 128)) ? 2 : 3;
     u32x4_t ka[KD][kFwdBN / 32];
     // Chunk 2c + g of row n sits at chunk (2c + g) ^ f(n); f < 16, so for c >= 8 (D = 256)
     // that is 16 + ((2(c - 8) + g) ^ f(n)): eight lane-dependent offsets and constants.
@@ -365,7 +377,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_tiled_kernel(
 template <typename T, int D, bool C, bool M, typename OutT>
 hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const float* sinks, const void* q, const void* k,
                         const void* v, void* o, float* lse, float scale, void* ws, hipStream_t st) {
-  const int n_qblk = (int)((s.Lq + kFwdBM - 1) / kFwdBM);
+  constexpr int BMW = 32 * fwd_waves<D, M>();
+  const int n_qblk = (int)((s.Lq + BMW - 1) / BMW);
   const int n_bh = (int)(s.B * s.Hq);
   const float scale_log2 = (float)((double)scale * 1.4426950408889634);
   constexpr int BN = fwd_bn<D, M>();
@@ -375,8 +388,8 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const float* s
   float* part_o = nsplit > 1 ? (float*)ws : nullptr;
   float* part_ml = nsplit > 1 ? part_o + (int64_t)nsplit * s.B * s.Hq * s.Lq * s.D : nullptr;
   // With key splits the sink joins in the combine kernel, once per row.
-  const size_t mshm = (M && mask_staged(mask)) ? 2 * (size_t)kFwdBM * BN : 0;  // staged mask blocks
-  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(kFwdThreads), mshm, st,
+  const size_t mshm = (M && mask_staged(mask)) ? 2 * (size_t)BMW * BN : 0;  // staged mask blocks
+  hipLaunchKernelGGL((fwd_tiled_kernel<T, D, C, M, OutT>), dim3(n_qblk * n_bh * nsplit), dim3(BMW * 2), mshm, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (OutT*)o, lse, (int)s.Hq,
                      (int)(s.Hq / s.Hkv), (int)s.Lq, (int)s.Lkv, n_qblk, n_bh, scale_log2, mask,
                      nsplit > 1 ? nullptr : sinks, nsplit, split_tiles, part_o, part_ml);
