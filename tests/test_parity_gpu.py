@@ -80,6 +80,10 @@ for _dt in ("f16", "bf16"):
         # head dim 256, forward and dQ keys split over 8 workgroups (16-row dQ waves)
         (1, 2, 1, 128, 1024, 256, _dt, False),  # 8 splits
         (1, 2, 2, 300, 1000, 256, _dt, True),   # 8 splits, causal with Lq < Lkv, last split empty
+        # head dim 128 without a mask: 8-wave forward workgroups of 256 rows, 128-key tiles,
+        # keys split over workgroups (ragged, causal with Lq < Lkv)
+        (1, 4, 2, 128, 2048, 128, _dt, False),
+        (1, 2, 1, 200, 1100, 128, _dt, True),
         # head dim 64 without a mask: 128-key forward tiles and 128-query dK/dV tiles
         (1, 4, 2, 200, 700, 64, _dt, True),     # causal with Lq < Lkv (tile starts rounded to 128)
         (2, 4, 4, 330, 330, 32, _dt, False),    # ragged last tiles, head dim 32
