@@ -987,34 +987,42 @@ __global__ __launch_bounds__(64 * kv_waves<D>(), 1) __attribute__((amdgpu_waves_
   }
 }
 
-// Splits of the two kernels (small grids only). dQ: as the forward, enough workgroups for
-// two per CU, at least 4 key tiles per split on average. dK/dV (one workgroup per CU):
-// enough for one per CU, at least 4 (head, query tile) steps per split. At most 16. Under a
-// causal mask dK/dV aims for two per CU: the key blocks near the end see few query tiles,
-// so about half of its split workgroups have little work (measured faster; the same for dQ
-// measured slower).
-int split_count(int64_t work, int64_t target, int64_t steps) {
+// Splits of the two kernels (small grids only), at most 16. dQ: enough workgroups for one
+// per CU, at least 4 key tiles per split on average; under a causal mask also at least one
+// split per 2048 keys (the longest row block sets the kernel's span), but no more than for
+// two workgroups per CU. dK/dV (one workgroup per CU): enough for one per CU, at least 8
+// (head, 64-query tile) steps per split; two per CU under a causal mask whose triangle spans
+// most of the keys (2 Lq > Lkv), where the key blocks near the end see few query tiles and
+// about half of the split workgroups have little work. (Measured on 8 and 16 heads of
+// 1024-4096 queries at D = 64-256 and GQA 8:1 at 1024 queries against 4096 keys: a second
+// workgroup per CU gains less than the fp32 partials and their reduction cost, except in those
+// two causal cases.)
+int split_count(int64_t work, int64_t target, int64_t steps, int64_t min_steps) {
   if (work >= target) return 1;
   int64_t n = (target + work - 1) / work;
-  if (n > steps / 4) n = steps / 4;
+  if (n > steps / min_steps) n = steps / min_steps;
   if (n > 16) n = 16;
   return n < 1 ? 1 : (int)n;
 }
-int dq_splits(const Shape& s) {
+int dq_splits(const Shape& s, bool causal) {
   const int64_t bn = s.D == 256 ? 32 : 64;
-  return split_count((s.Lq + kDqBM - 1) / kDqBM * s.B * s.Hq, 2 * 256, (s.Lkv + bn - 1) / bn);
+  const int64_t work = (s.Lq + kDqBM - 1) / kDqBM * s.B * s.Hq, steps = (s.Lkv + bn - 1) / bn;
+  const int n = split_count(work, 256, steps, 4);
+  if (!causal) return n;
+  return min(split_count(work, 2 * 256, steps, 4), max(n, (int)((s.Lkv + 2047) / 2048)));
 }
 int dkv_splits(const Shape& s, bool causal) {
   const int64_t bn = 128;  // 8 waves x 16 keys
-  return split_count((s.Lkv + bn - 1) / bn * s.B * s.Hkv, (causal ? 2 : 1) * 256,
-                     (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM));
+  const bool triangle = causal && 2 * s.Lq > s.Lkv;
+  return split_count((s.Lkv + bn - 1) / bn * s.B * s.Hkv, (triangle ? 2 : 1) * 256,
+                     (s.Hq / s.Hkv) * ((s.Lq + kKvBM - 1) / kKvBM), 8);
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Workspace: {LSE*log2e, -Delta} pairs, then (split grids) the dQ partials, then the dK and
 // dV partials.
 size_t rowstat_bytes(const Shape& s) { return align256((size_t)(s.B * s.Hq * tiled_rowstat_stride(s.Lq)) * 8); }
-size_t dq_part_bytes(const Shape& s) {
-  const int n = dq_splits(s);
+size_t dq_part_bytes(const Shape& s, bool causal) {
+  const int n = dq_splits(s, causal);
   return n > 1 ? align256((size_t)n * (size_t)(s.B * s.Hq * s.Lq * s.D) * 4) : 0;
 }
 size_t dkv_part_bytes(const Shape& s, bool causal) {  // each of dK, dV
@@ -1034,7 +1042,7 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q,
   if (stages & kStage0) {
     const int n_qblk = (int)((s.Lq + kDqBM - 1) / kDqBM);
     const int n_bh = (int)(s.B * s.Hq);
-    const int nsplit = dq_splits(s);
+    const int nsplit = dq_splits(s, C);
     constexpr int BN = dq_bn<D, M>();
     const int nt = (int)((s.Lkv + BN - 1) / BN);
     float* dq_part = nsplit > 1 ? (float*)parts : nullptr;
@@ -1058,8 +1066,8 @@ hipError_t launch_typed(const Shape& s, Dt out, const Mask& mask, const void* q,
   const int n_kblk = (int)((s.Lkv + kKvBN - 1) / kKvBN);
   const int n_bhk = (int)(s.B * s.Hkv);
   const int nsplit = dkv_splits(s, C);
-  float* dk_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s)) : nullptr;
-  float* dv_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s) + dkv_part_bytes(s, C)) : nullptr;
+  float* dk_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s, C)) : nullptr;
+  float* dv_part = nsplit > 1 ? (float*)(parts + dq_part_bytes(s, C) + dkv_part_bytes(s, C)) : nullptr;
   auto kern = nsplit > 1 ? dkv_kernel<T, D, C, M, OutT, true> : dkv_kernel<T, D, C, M, OutT, false>;
   hipLaunchKernelGGL(kern, dim3(n_kblk * n_bhk * nsplit), dim3(64 * kv_waves<D>()), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dO, (const f32x2_t*)rowstat, (OutT*)dk,
@@ -1104,7 +1112,7 @@ hipError_t launch_d(const Shape& s, Dt out, bool causal, const Mask& mask, const
 }  // namespace
 
 size_t tiled_bwd_workspace(const Shape& s, bool causal) {
-  return rowstat_bytes(s) + dq_part_bytes(s) + 2 * dkv_part_bytes(s, causal);
+  return rowstat_bytes(s) + dq_part_bytes(s, causal) + 2 * dkv_part_bytes(s, causal);
 }
 
 hipError_t launch_bwd_tiled(const Shape& s, Dt dt, Dt out, bool causal, const Mask& mask, const void* q,

@@ -41,7 +41,6 @@
 namespace sdpa {
 namespace {
 
-constexpr int kFwdBM = 128;  // query rows per 4-wave workgroup (the key-split count's unit)
 // Keys per tile: 64, or 32 at D = 256, where the O accumulators alone take 128 registers
 // per lane and a 64-key score block would not fit beside them. Every head dim runs two
 // waves per SIMD: at D = 256 that leaves 256 registers per lane for 128 of accumulators
@@ -422,15 +421,19 @@ hipError_t launch_d(const Shape& s, Dt out, bool causal, const Mask& mask, const
 
 }  // namespace
 
-// Key splits: enough workgroups for two per CU (256 CUs), each split keeping at least 4 key
-// tiles of 64 keys on average (counted in 64-key tiles whatever the instantiation's tile, so
-// that the count, and the workspace, do not depend on the mask), at most 16 splits. (Doubling the target under a causal mask, where about
-// half of the split workgroups have little work, measured slower at one batch of 8 heads,
-// L = 2048: the partials cost more than the shorter critical path saves.)
+// Key splits (small grids only): enough workgroups for one per CU (256 CUs), counted in the
+// workgroups the unmasked instantiation launches (256 query rows at D = 128, 128 otherwise),
+// and for two per CU at D = 256; each split keeps at least 4 key tiles of 64 keys on average
+// (counted in 64-key tiles whatever the instantiation's tile, so that the count, and the
+// workspace, do not depend on the mask); at most 16 splits. At D <= 96 a second 4-wave
+// workgroup per CU gains less than its fp32 partials and their combine cost (measured on 8
+// and 16 heads of 1024-4096 queries, fp16 D = 64: 8 heads of 2048 take 22 us with two splits
+// against 26 us with four); at D = 256 the longer tiles make the second one pay.
 int tiled_fwd_splits(const Shape& s) {
   const int64_t bn = s.D == 256 ? 32 : 64;
-  const int64_t work = (s.Lq + kFwdBM - 1) / kFwdBM * s.B * s.Hq;
-  const int64_t target = 2 * 256;
+  const int64_t rows = s.D == 128 ? 256 : 128;
+  const int64_t work = (s.Lq + rows - 1) / rows * s.B * s.Hq;
+  const int64_t target = s.D == 256 ? 2 * 256 : 256;
   if (work >= target) return 1;
   const int64_t nt = (s.Lkv + bn - 1) / bn;
   int64_t n = (target + work - 1) / work;

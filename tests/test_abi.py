@@ -56,19 +56,21 @@ def test_workspace_sizes():
     # backward keeps Delta (fp32 per query row)
     assert sd.workspace_bytes(0, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) == 0
     assert sd.workspace_bytes(0, 8, 8, 8, 128, 128, 64, False, sd.F32) == 0
-    # small tiled grids split the keys: fp32 partials O [nsplit, B*Hq*Lq, D] and (m, l)
-    assert sd.workspace_bytes(0, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == 4 * 8 * 2048 * (64 + 2) * 4
-    assert sd.workspace_bytes(0, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == 2 * 8 * 4096 * (64 + 2) * 4
-    # causal dK/dV splits aim for two workgroups per CU: L = 4096 now splits its query tiles 2 ways
+    # small tiled grids split the keys: fp32 partials O [nsplit, B*Hq*Lq, D] and (m, l), with
+    # enough splits for one 128-row workgroup per CU at D = 64 (8 heads of 2048 rows: 2)
+    assert sd.workspace_bytes(0, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == 2 * 8 * 2048 * (64 + 2) * 4
+    assert sd.workspace_bytes(0, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == 0  # 256 workgroups: no split
+    # a causal dQ on a small grid keeps one split per 2048 keys (here 2), and causal dK/dV aims for
+    # two workgroups per CU: L = 4096 splits its query tiles 2 ways
     rows = 8 * 4096
     assert sd.workspace_bytes(1, 1, 8, 8, 4096, 4096, 64, True, sd.F16) == rows * 8 + 2 * rows * 64 * 4 + 2 * (
         2 * rows * 64 * 4)
-    assert sd.workspace_bytes(1, 1, 8, 8, 4096, 4096, 64, False, sd.F16) == rows * 8 + 2 * rows * 64 * 4
+    assert sd.workspace_bytes(1, 1, 8, 8, 4096, 4096, 64, False, sd.F16) == rows * 8
     assert sd.workspace_bytes(0, 1, 2, 2, 200, 200, 64, True, sd.F16) == 0  # too few key tiles to split
-    # ... and so does the backward: {LSE*log2e, Delta} pairs, dQ partials (4 key splits), dK and dV
+    # ... and so does the backward: {LSE*log2e, Delta} pairs, dQ partials (2 key splits), dK and dV
     # partials (2 splits of the query tiles)
     rows, kv = 8 * 2048, 8 * 2048
-    assert sd.workspace_bytes(1, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == rows * 8 + 4 * rows * 64 * 4 + 2 * (
+    assert sd.workspace_bytes(1, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == rows * 8 + 2 * rows * 64 * 4 + 2 * (
         2 * kv * 64 * 4)
     assert sd.workspace_bytes(1, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) >= 4 * 32 * 4096 * 4
     assert sd.workspace_bytes(1, 8, 8, 8, 128, 128, 64, False, sd.F32) >= 8 * 8 * 128 * 4

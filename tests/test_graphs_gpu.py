@@ -20,7 +20,7 @@ CASES = [
     (1, 8, 2, 200, 200, 128, "bf16", True, False),   # tiled
     (2, 8, 2, 8, 3000, 64, "bf16", False, True),      # short-query, several splits
     (1, 4, 2, 70, 130, 64, "f16", False, True),       # tiled with a mask
-    (1, 4, 1, 256, 1024, 64, "f16", False, True),     # tiled, small grid: every kernel split 4 ways
+    (1, 4, 1, 256, 1024, 64, "f16", False, True),     # tiled, small grid: forward and dQ split 4 ways, dK/dV 2
     (1, 2, 2, 40, 60, 32, "f32", True, False),        # float32 path
     (1, 4, 2, 130, 260, 256, "f16", True, False),     # head dim 256: two-wave forward, 16-row dQ
     (1, 4, 2, 150, 300, 256, "bf16", False, True),    # head dim 256 with a mask (the forward spills registers)

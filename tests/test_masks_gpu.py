@@ -43,7 +43,7 @@ for _dt in ("f16", "bf16"):
         (2, 4, 2, 100, 132, 64, _dt, False, "bool", "head", 0, True),        # per-head block, staged
         (2, 4, 2, 90, 200, 128, _dt, False, "bool", "full", 0, False),       # per-(batch, head) block
         (1, 2, 1, 100, 800, 64, _dt, True, None, None, 0, True),             # causal + sinks, 3 key splits
-        (1, 8, 2, 256, 300, 128, _dt, False, "bool", "keypad", 0, True),     # dK/dV in 4 splits
+        (1, 8, 2, 256, 300, 128, _dt, False, "bool", "keypad", 0, True),     # dK/dV in 2 splits
         # contiguous key padding (batch b keeps its first keys, one batch none): whole key
         # tiles and whole dK/dV waves are padding, which the tiled kernels skip
         (3, 4, 2, 130, 600, 128, _dt, False, "bool", "padded", 0, False),

@@ -65,8 +65,10 @@ for _dt in ("f16", "bf16"):
         (1, 2, 2, 640, 640, 64, _dt, True),     # 2 splits, the second empty for the first query blocks
         (1, 2, 1, 96, 700, 96, _dt, False),     # 2 splits, head dim 96
         # backward splits on small grids: dK/dV over its (query head, query tile) sequence
-        (1, 8, 1, 512, 256, 64, _dt, False),    # 16 splits, GQA 8:1
-        (1, 4, 1, 256, 200, 256, _dt, False),   # 4 splits, head dim 256
+        (1, 8, 1, 512, 256, 64, _dt, False),    # 8 splits, GQA 8:1
+        (1, 4, 1, 256, 200, 256, _dt, False),   # 2 splits, head dim 256
+        (1, 4, 1, 512, 512, 128, _dt, True),    # causal, 4 splits
+        (1, 4, 1, 500, 512, 64, _dt, True),     # causal, 4 splits, ragged last query tile
         # head dim 256 (32-key forward / dQ tiles, 16-row dQ waves, dK/dV with K rows in LDS and
         # 32-query tiles, 2-wave short-query kernels)
         (1, 4, 2, 200, 200, 256, _dt, True),    # tiled, causal
