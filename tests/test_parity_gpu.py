@@ -90,6 +90,9 @@ for _dt in ("f16", "bf16"):
         (1, 4, 2, 200, 700, 64, _dt, True),     # causal with Lq < Lkv (tile starts rounded to 128)
         (2, 4, 4, 330, 330, 32, _dt, False),    # ragged last tiles, head dim 32
     ]
+# A causal dQ on a small grid: one key split per 2048 keys binds (3 splits where one workgroup
+# per CU would take 2).
+CASES += [(1, 4, 4, 4100, 4100, 32, "bf16", True)]
 
 
 def _id(c):
