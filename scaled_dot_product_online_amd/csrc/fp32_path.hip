@@ -4,12 +4,12 @@
 // scaled-dot-product-attention pattern ...", "Reproducer + metrics": B=8, H=8,
 // S=128, D=64) and their stated accuracy is 1e-5 ("Acceptance criteria"), so this
 // path keeps every product and sum in fp32 and runs on the VALUs: R lanes share one
-// row, each holding a W-element slice (W = 4 up to D = 128: short per-lane chains and a
-// large grid for these small shapes; W = 8 at D = 256, where R = 32 is the most a row's
-// lane sum takes; R = 8 lanes of 12 at D = 96 so that R stays a power of two). It follows
-// the same online softmax (exp2 domain) and the same two-kernel backward without atomics
-// as the 16-bit path (MLX pull request "[Metal] Add Flash Attention VJP for training",
-// "Implementation Notes").
+// row, each holding a W-element slice (W = 2 at D = 32 and 4 at D = 64 and 128: short
+// per-lane chains and a large grid for these small shapes; W = 8 at D = 256, where R = 32
+// is the most a row's lane sum takes; R = 8 lanes of 12 at D = 96 so that R stays a power
+// of two). It follows the same online softmax (exp2 domain) and the same two-kernel
+// backward without atomics as the 16-bit path (MLX pull request "[Metal] Add Flash
+// Attention VJP for training", "Implementation Notes").
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,7 +38,7 @@ __device__ __forceinline__ float row_sum(float x) {
 // of a row (reading different slices of the same row) hit different banks.
 template <int D>
 struct F32Tile {
-  static constexpr int R = (D == 96) ? 8 : (D <= 128 ? D / 4 : D / 8);  // lanes per row
+  static constexpr int R = D == 96 ? 8 : D == 256 ? 32 : D == 32 ? 16 : D / 4;  // lanes per row
   static constexpr int W = D / R;                   // elements of a lane's slice
   static constexpr int SP = W + 1;                  // slice pitch in LDS
   static constexpr int PITCH = R * SP;
