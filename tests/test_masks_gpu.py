@@ -60,6 +60,9 @@ CASES += [
     (2, 4, 1, 20, 50, 32, "f32", False, "additive", "shared", 0, False),
     (1, 2, 1, 30, 30, 128, "f32", True, None, None, 0, True),
     (1, 2, 1, 24, 40, 256, "f32", False, "additive", "head", 1, True),
+    # float32 rows of 32 lanes (D = 128) and of 16 two-element slices (D = 32)
+    (1, 4, 2, 45, 70, 128, "f32", False, "bool", "keypad", 1, True),
+    (2, 2, 1, 33, 90, 32, "f32", False, "bool", "full", 2, False),
 ]
 
 
