@@ -104,8 +104,8 @@ int sdpa_select_path(int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lkv, int64_t D
  * pages' kernels take the caller's tensors' buffers directly (mps-flash-sdpa 0.1.0,
  * "How It Works": zero-copy buffer handoff to the kernels). Returns (size_t)-1 when the
  * sizes are invalid. The forward needs one on the short-query path, and on the
- * tiled path when its grid of (128-query block, head) pairs is too small to give
- * every compute unit two workgroups: there the keys are split over several
+ * tiled path when its grid of (query block, head) pairs is too small to give every
+ * compute unit a workgroup (two at D = 256): there the keys are split over several
  * workgroups whose fp32 partials (unnormalised O, running max, row sum) the
  * workspace holds until a second kernel merges them. The backward always needs one
  * (per-row statistics that its first stage leaves for the second); on small grids
