@@ -72,6 +72,16 @@ def test_workspace_sizes():
     rows, kv = 8 * 2048, 8 * 2048
     assert sd.workspace_bytes(1, 1, 8, 8, 2048, 2048, 64, False, sd.F16) == rows * 8 + 2 * rows * 64 * 4 + 2 * (
         2 * kv * 64 * 4)
+    # a causal dQ on a small grid keeps one key split per 2048 keys: 4 heads of 4100 rows (132
+    # workgroups) take 3 splits, not the 2 of one workgroup per CU; dK/dV aims for two workgroups
+    # per CU there (2 Lq > Lkv): 4 splits of its 65 query tiles
+    rows = 4 * 4100
+    assert sd.workspace_bytes(1, 1, 4, 4, 4100, 4100, 32, True, sd.BF16) == 4 * 4160 * 8 + 3 * rows * 32 * 4 + 2 * (
+        4 * rows * 32 * 4)
+    # ... and only one per CU where the causal triangle is short (1024 queries against 4096
+    # keys): dQ 4 splits, dK/dV 8 of its 32 workgroups
+    assert sd.workspace_bytes(1, 1, 8, 1, 1024, 4096, 128, True, sd.BF16) == 8 * 1024 * 8 + 4 * 8 * 1024 * 128 * 4 + 2 * (
+        8 * 4096 * 128 * 4)
     assert sd.workspace_bytes(1, 4, 32, 4, 4096, 4096, 128, True, sd.BF16) >= 4 * 32 * 4096 * 4
     assert sd.workspace_bytes(1, 8, 8, 8, 128, 128, 64, False, sd.F32) >= 8 * 8 * 128 * 4
     # vector path: split partials
