@@ -5,7 +5,8 @@ The shapes are drawn once from a fixed generator: operand type, head dim (32 to 
 GQA group size (1 to 8), causal or not, query lengths from 1 (short-query path) to a
 few hundred, and key lengths up to about 1200, so that most cases have ragged tails and
 many run on grids small enough for the kernels to split their keys or query tiles
-across workgroups. Sizes stay where the oracle finishes in about a second.
+across workgroups. A second draw adds long causal shapes on small grids. Sizes stay where
+the oracle finishes in a few seconds.
 """
 
 import numpy as np
@@ -36,6 +37,28 @@ def _draw_cases(n, seed=2026, max_work=1.5e8):
 
 
 CASES = _draw_cases(32)
+
+
+def _draw_long_causal(n, seed=2027, max_work=6e8):
+    """Causal 16-bit shapes of 600-2600 queries against up to 1500 more keys on one batch of
+    1-8 heads: small grids where the forward and dQ split their keys (the causal dQ at least
+    once per 2048 keys) and dK/dV its query tiles, with long and short causal triangles."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dt = str(rng.choice(["f16", "bf16"]))
+        D = int(rng.choice([32, 64, 128]))
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.choice([1, 2, 4]))
+        Lq = int(rng.integers(600, 2600))
+        Lkv = int(rng.integers(Lq, Lq + 1500))
+        if Hkv * G * Lq * Lkv * D > max_work:
+            continue
+        cases.append((1, Hkv * G, Hkv, Lq, Lkv, D, dt, True))
+    return cases
+
+
+CASES += _draw_long_causal(12)
 
 
 def _id(c):
